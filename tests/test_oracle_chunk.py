@@ -1,0 +1,108 @@
+"""Pins for the chunk relative-L1 / reuse-decision half of the oracle (CPU).
+
+Definitions: "Flow Caching for Autoregressive Video Generation" (papernotes
+digest), Key designs item 1 (chunk relative L1) and item 2 (chunkwise
+adaptive caching with accumulator f, m forced steps and threshold eps).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_compression_fc_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_chunk(l1_seq, m, eps):
+    f, rec, fs = 0.0, [], []
+    for n, l1 in enumerate(l1_seq):
+        r, f = oracle.decide(n, f, l1, m, eps)
+        rec.append(int(r)); fs.append(f)
+    return rec, fs
+
+
+def test_hand_worked_sequence():
+    g = json.load(open(os.path.join(GOLDEN, "decision_hand_example.json")))
+    rec, fs = run_chunk(g["l1_rel"], g["m"], g["eps"])
+    assert rec == g["expect_recompute"]
+    np.testing.assert_allclose(fs, g["expect_f"], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("m", [0, 1, 3, 5])
+def test_first_m_steps_forced(m):
+    rec, fs = run_chunk([1e-9] * 12, m, 0.01)
+    assert rec[:m] == [1] * m and fs[:m] == [0.0] * m
+    assert rec[m:] == [0] * (12 - m)
+
+
+@pytest.mark.parametrize("c,eps", [(0.004, 0.01), (0.003, 0.01), (0.006, 0.015), (0.02, 0.015)])
+def test_constant_l1_period(c, eps):
+    # after the forced steps the pattern repeats floor(eps/c) reuses then one recompute
+    m = 2
+    rec, _ = run_chunk([c] * 40, m, eps)
+    k = math.floor(eps / c)
+    period = [0] * k + [1]
+    tail = rec[m:]
+    assert tail == (period * 40)[:len(tail)]
+
+
+def test_f_stays_in_range():
+    rng = np.random.default_rng(0)
+    l1 = rng.exponential(0.004, size=500)
+    _, fs = run_chunk(l1, 3, 0.01)
+    assert all(0.0 <= f <= 0.01 for f in fs)
+
+
+def test_strict_threshold():
+    # a == eps reuses ("f <= eps -> reuse"); just above recomputes
+    assert oracle.decide(5, 0.25, 0.25, 2, 0.5) == (False, 0.5)
+    assert oracle.decide(5, 0.25, 0.2500001, 2, 0.5)[0] is True
+
+
+def test_l1_rel_definition_and_zero_norm():
+    x_t = np.array([1.0, -2.0, 3.0, 0.0, 0.0, 4.0])
+    x_tm1 = np.array([1.5, -2.0, 2.0, 1.0, -1.0, 4.0])
+    got = oracle.chunk_l1_rel(x_t, x_tm1, [0, 3, 5, 6])
+    np.testing.assert_allclose(got[0], (0.5 + 0 + 1.0) / 6.0, rtol=1e-15)
+    assert got[1] == np.inf                       # ||X_t||_1 = 0
+    assert got[2] == 0.0
+    r, _ = oracle.decide(4, 0.0, got[1], 2, 0.01)
+    assert r is True
+
+
+def test_tiny_trajectory_closed_form():
+    # X_{t-1} - X_t = -v (sigma(t) - sigma(t-1)) exactly, so the numerator is
+    # (sigma(t) - sigma(t-1)) * ||v||_1 up to the generator's float32 rounding.
+    cfg = synth.CHUNK_CONFIGS["tiny"]
+    tr = synth.ChunkTrajectory(cfg, seed=0)
+    for g in range(tr.n_global_steps()):
+        xt, xtm1, steps = tr.pair(g)
+        A, Nrm = oracle.chunk_l1_sums(xt, xtm1, tr.offsets)
+        for i, n in enumerate(steps):
+            t = cfg.N - n
+            dsig = tr.sigma(t) - tr.sigma(t - 1)
+            want = dsig * np.abs(tr.v[i].astype(np.float64)).sum()
+            np.testing.assert_allclose(A[i], want, rtol=2e-6)
+            np.testing.assert_allclose(Nrm[i], np.abs(tr.state_f32(i, t).astype(np.float64)).sum(), rtol=0)
+
+
+def test_resume_from_checkpoint():
+    # the only state is (f, local step): stopping after k steps and restarting
+    # from the saved pair gives the same decisions
+    rng = np.random.default_rng(1)
+    l1 = list(rng.exponential(0.005, size=50))
+    full, _ = run_chunk(l1, 5, 0.01)
+    for k in (3, 5, 17, 49):
+        f = 0.0
+        rec = []
+        for n in range(k):
+            r, f = oracle.decide(n, f, l1[n], 5, 0.01); rec.append(int(r))
+        saved = (k, f)
+        n0, f = saved
+        for n in range(n0, 50):
+            r, f = oracle.decide(n, f, l1[n], 5, 0.01); rec.append(int(r))
+        assert rec == full
