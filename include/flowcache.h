@@ -1,0 +1,210 @@
+/*
+ * flowcache.h -- C ABI of libflowcache.so: the FlowCache per-step hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is described on the page "Flow Caching for Autoregressive Video
+ * Generation" (papernotes.org ICLR 2026 digest), section 方法详解 / 关键设计
+ * ("Key designs"):
+ *   item 1  chunk relative L1 distance  L1_rel = ||X_{t-1} - X_t||_1 / ||X_t||_1;
+ *   item 2  chunkwise adaptive caching: accumulator f, forced recompute for the
+ *           first m steps, recompute-and-reset when f + L1_rel > eps, else reuse;
+ *   item 3  joint importance-redundancy KV-cache compression:
+ *           Imp~ = max-pool_1d( mean_i softmax_j(scale q_i.k_j) ),
+ *           Red_j = softmax_j( (1/L_k) sum_{i != j} khat_i.khat_j ),
+ *           Score_j = lambda Imp~_j - (1 - lambda) Red_j, and each head keeps
+ *           its top-B tokens (flowchart under 整体框架: cache full -> score ->
+ *           top-B per head; not full -> keep as is).
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to memory of the current
+ *     HIP device; host pointers are read before the call returns.
+ *   - The caller owns all memory.  The library never allocates or frees; any
+ *     temporary storage is the caller's workspace, sized by the *_bytes query.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and runs asynchronously.  Argument checks happen on the host, before
+ *     anything is queued, and return an error code synchronously.
+ *   - Outputs must not alias inputs.  Tensors are dense and row-contiguous.
+ *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
+ *     in [0,1], even pool window, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
+ *     128, unknown dtype, too many chunks), FC_ERR_WORKSPACE (workspace null or
+ *     smaller than the query), FC_ERR_HIP (a launch failed).  No exception
+ *     crosses the ABI.  NaN/Inf inputs are not supported.
+ *   - The library keeps no state between calls; calls on different streams
+ *     with different workspaces may run concurrently.
+ */
+#ifndef FLOWCACHE_H
+#define FLOWCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FC_OK = 0,
+    FC_ERR_INVALID_ARG = 1,
+    FC_ERR_UNSUPPORTED = 2,
+    FC_ERR_WORKSPACE = 3,
+    FC_ERR_HIP = 4
+} fc_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* fc_status_string(fc_status s);
+
+/* Element type of Q, K, V, K_out, V_out and of the chunk states. */
+typedef enum { FC_F32 = 0, FC_BF16 = 1 } fc_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Joint importance-redundancy KV compression (Key designs, item 3)         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Parameters in the page's notation.
+ *   H            heads (every head is compressed independently)
+ *   d            head dimension, 64 or 128
+ *   L_q          denoising queries (the active chunk's tokens)
+ *   L_k          clean keys in the cache before compression
+ *   B_budget     tokens each head keeps; B' = min(B_budget, L_k)
+ *   lambda       importance weight in [0,1]
+ *   pool_window  odd max-pool window w >= 1 (stride 1, same size, positions
+ *                outside [0, L_k) ignored, along the token order)
+ *   softmax_scale attention temperature; 0 means 1/sqrt(d)
+ *   dtype        FC_BF16 or FC_F32 for Q, K, V and K_out, V_out
+ */
+typedef struct {
+    int32_t H, d, L_q, L_k, B_budget;
+    float lambda;
+    int32_t pool_window;
+    float softmax_scale;
+    fc_dtype dtype;
+} fc_kv_params;
+
+/* Workspace bytes that fc_kv_compress, fc_kv_importance, fc_kv_redundancy and
+ * fc_kv_select need for these parameters (0 if the parameters are invalid). */
+size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
+
+/*
+ * fc_kv_compress -- the whole compression step for all heads.
+ *   Q [H][L_q][d], K [H][L_k][d], V [H][L_k][d]       device, dtype
+ *   K_out, V_out [H][B'][d]                           device, dtype; the rows
+ *                                                     of the kept tokens, in
+ *                                                     ascending token order
+ *   idx_out [H][B']  int32                            device; kept token
+ *                                                     indices, ascending
+ *   score_out, imp_pooled_out, red_out [H][L_k] f32   device, nullable: the
+ *                                                     joint score, the pooled
+ *                                                     importance, the
+ *                                                     redundancy softmax
+ *   workspace                                         device, >= the query
+ * Selection order: larger score first; equal scores keep the lower index.
+ * L_k <= B_budget keeps every token (idx = 0..L_k-1).  Zero-norm keys are
+ * normalised with max(||k||, 1e-12) and so contribute no similarity.
+ * Deterministic: identical inputs give bit-identical outputs.
+ */
+fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, const void* V,
+                         void* K_out, void* V_out, int32_t* idx_out,
+                         float* score_out, float* imp_pooled_out, float* red_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_importance -- importance before the pool:
+ *   imp_out[h][j] = (1/L_q) sum_i exp(s_ij - lse_i),  s_ij = scale q_i.k_j,
+ *   lse_i = log sum_j exp(s_ij)  (softmax over the clean keys only).
+ * Q, K device (dtype); imp_out [H][L_k] f32 device.  Uses p->H, d, L_q, L_k,
+ * softmax_scale, dtype.
+ */
+fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, float* imp_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_redundancy -- mean cosine similarity before its softmax:
+ *   r_out[h][j] = (1/L_k) sum_{i != j} khat_i.khat_j,  khat = k / max(||k||, 1e-12),
+ * computed as (u.khat_j - khat_j.khat_j)/L_k with u = sum_i khat_i (no L_k^2
+ * matrix).  K device (dtype); r_out [H][L_k] f32 device.  Uses p->H, d, L_k,
+ * dtype.
+ */
+fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_select -- pool, score, top-B and gather from given importance and
+ * redundancy means:
+ *   imp [H][L_k] f32 device (before the pool), r [H][L_k] f32 device (before
+ *   the softmax).  Red = softmax_j(r), Imp~ = max-pool(imp), Score as above.
+ *   K, V, K_out, V_out may all be NULL (indices only); otherwise all four are
+ *   required.  Other outputs as for fc_kv_compress.
+ */
+fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r,
+                       const void* K, const void* V, void* K_out, void* V_out, int32_t* idx_out,
+                       float* score_out, float* imp_pooled_out, float* red_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for fc_topb_select. */
+size_t fc_topb_select_workspace_bytes(int32_t H, int32_t L);
+
+/*
+ * fc_topb_select -- per row h of scores [H][L] (f32, device), the
+ * B' = min(B, L) largest values, ties to the lower index, written to
+ * idx_out [H][B'] (int32, device) in ascending index order.  -0.0 and +0.0
+ * are equal.  Exact: the result is a function of the float32 values only.
+ */
+fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, int32_t* idx_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Chunkwise relative L1 and reuse decision (Key designs, items 1 and 2)    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ *   n_chunks  chunks in the flat state arrays, 1..FC_MAX_CHUNKS
+ *   m         forced-recompute steps counted from each chunk's first step
+ *   eps       reuse threshold
+ *   dtype     FC_BF16 or FC_F32 for the states
+ */
+#define FC_MAX_CHUNKS 128
+typedef struct {
+    int32_t n_chunks;
+    int32_t m;
+    float eps;
+    fc_dtype dtype;
+} fc_l1_params;
+
+/* Workspace bytes for these chunk offsets (host array of n_chunks+1). */
+size_t fc_chunk_rel_l1_workspace_bytes(const fc_l1_params* p, const int64_t* chunk_offsets);
+
+/* Zero a chunk-L1 workspace (device) on `stream`.  Needed once before its
+ * first use; every fc_chunk_rel_l1_decide leaves it zeroed again. */
+fc_status fc_chunk_rel_l1_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_chunk_rel_l1_decide -- one denoising step's decision for every chunk.
+ *   chunk_offsets  host int64[n_chunks+1], element offsets into the states,
+ *                  non-decreasing, chunk i = [off[i], off[i+1]), off[0] >= 0
+ *   X_t, X_tm1     device, dtype: the current state X_t and the next state
+ *                  X_{t-1}, chunks concatenated
+ *   step           device int32[n_chunks] in/out: each chunk's local step n
+ *                  (0 on its first step); < 0 marks an inactive chunk, whose
+ *                  elements are not read and whose outputs are left untouched
+ *   f              device f32[n_chunks] in/out: the accumulator
+ *   recompute      device uint8[n_chunks] out: 1 = recompute, 0 = reuse
+ *   l1_rel_out     device f32[n_chunks], nullable: L1_rel of this step
+ *                  (+inf when ||X_t||_1 = 0)
+ * For an active chunk with local step n:
+ *   n < m:  recompute = 1, f = 0;
+ *   else a = f + L1_rel;  a > eps: recompute = 1, f = 0;  else recompute = 0, f = a;
+ *   then step = n + 1.
+ * Sums are taken in float32 per thread and combined in a fixed order
+ * (deterministic); the decision runs on the device, with no host round trip.
+ * The workspace must have been zeroed once (fc_chunk_rel_l1_workspace_init).
+ */
+fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets,
+                                 const void* X_t, const void* X_tm1,
+                                 int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLOWCACHE_H */

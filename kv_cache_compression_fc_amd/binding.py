@@ -1,0 +1,258 @@
+"""Thin Python binding of libflowcache.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU, passes their device pointers and the
+current HIP stream through ctypes, and raises ``FlowCacheError`` on a non-OK
+status.  torch provides device memory and streams; all arithmetic runs in the
+library's HIP kernels.  Importing this module loads the library and fails
+loudly when it has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflowcache.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python kv_cache_compression_fc_amd/csrc/build.py). There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FC_OK, FC_ERR_INVALID_ARG, FC_ERR_UNSUPPORTED, FC_ERR_WORKSPACE, FC_ERR_HIP = range(5)
+FC_F32, FC_BF16 = 0, 1
+FC_MAX_CHUNKS = 128
+
+EXPORTS = (
+    "fc_status_string", "fc_kv_compress_workspace_bytes", "fc_kv_compress", "fc_kv_importance",
+    "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
+    "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_workspace_init", "fc_chunk_rel_l1_decide",
+)
+
+
+class fc_kv_params(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("L_q", ctypes.c_int32),
+                ("L_k", ctypes.c_int32), ("B_budget", ctypes.c_int32), ("lambda_", ctypes.c_float),
+                ("pool_window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
+
+
+class fc_l1_params(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int32), ("m", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
+
+
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_lib.fc_status_string.restype = ctypes.c_char_p
+_lib.fc_status_string.argtypes = [ctypes.c_int]
+_lib.fc_kv_compress_workspace_bytes.restype = _sz
+_lib.fc_kv_compress_workspace_bytes.argtypes = [ctypes.POINTER(fc_kv_params)]
+_lib.fc_kv_compress.restype = ctypes.c_int
+_lib.fc_kv_compress.argtypes = [ctypes.POINTER(fc_kv_params)] + [_vp] * 9 + [_vp, _sz, _vp]
+_lib.fc_kv_importance.restype = ctypes.c_int
+_lib.fc_kv_importance.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_kv_redundancy.restype = ctypes.c_int
+_lib.fc_kv_redundancy.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _sz, _vp]
+_lib.fc_kv_select.restype = ctypes.c_int
+_lib.fc_kv_select.argtypes = [ctypes.POINTER(fc_kv_params)] + [_vp] * 10 + [_vp, _sz, _vp]
+_lib.fc_topb_select_workspace_bytes.restype = _sz
+_lib.fc_topb_select_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+_lib.fc_topb_select.restype = ctypes.c_int
+_lib.fc_topb_select.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_chunk_rel_l1_workspace_bytes.restype = _sz
+_lib.fc_chunk_rel_l1_workspace_bytes.argtypes = [ctypes.POINTER(fc_l1_params), _i64p]
+_lib.fc_chunk_rel_l1_workspace_init.restype = ctypes.c_int
+_lib.fc_chunk_rel_l1_workspace_init.argtypes = [_vp, _sz, _vp]
+_lib.fc_chunk_rel_l1_decide.restype = ctypes.c_int
+_lib.fc_chunk_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]
+
+
+class FlowCacheError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {fc_status_string(status)} (status {status})")
+        self.status = status
+
+
+def fc_status_string(status: int) -> str:
+    return _lib.fc_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != FC_OK:
+        raise FlowCacheError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FC_BF16
+    if t.dtype == torch.float32:
+        return FC_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def kv_params(Q: torch.Tensor, K: torch.Tensor, B_budget: int, lam: float, pool_window: int,
+              softmax_scale: float = 0.0) -> fc_kv_params:
+    H, Lq, d = Q.shape
+    return fc_kv_params(H, d, Lq, K.shape[1], int(B_budget), float(lam), int(pool_window),
+                        float(softmax_scale), _dtype_code(K))
+
+
+def fc_kv_compress_workspace_bytes(p: fc_kv_params) -> int:
+    return int(_lib.fc_kv_compress_workspace_bytes(ctypes.byref(p)))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def fc_kv_compress(Q, K, V, B_budget: int, lam: float, pool_window: int, softmax_scale: float = 0.0,
+                   want_scores: bool = False, out: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """Whole compression step.  Returns K_out, V_out, idx (+ score,
+    imp_pooled, red when want_scores).  ``out`` may hold preallocated outputs."""
+    p = kv_params(Q, K, B_budget, lam, pool_window, softmax_scale)
+    H, Lk, d = K.shape
+    Bp = min(int(B_budget), Lk)
+    out = dict(out or {})
+    dev = K.device
+    out.setdefault("K_out", torch.empty((H, Bp, d), dtype=K.dtype, device=dev))
+    out.setdefault("V_out", torch.empty((H, Bp, d), dtype=V.dtype, device=dev))
+    out.setdefault("idx", torch.empty((H, Bp), dtype=torch.int32, device=dev))
+    if want_scores:
+        for k in ("score", "imp_pooled", "red"):
+            out.setdefault(k, torch.empty((H, Lk), dtype=torch.float32, device=dev))
+    nbytes = fc_kv_compress_workspace_bytes(p)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("fc_kv_compress", _lib.fc_kv_compress(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(out["K_out"]), _ptr(out["V_out"]), _ptr(out["idx"]),
+        _ptr(out.get("score")), _ptr(out.get("imp_pooled")), _ptr(out.get("red")),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def fc_kv_importance(Q, K, softmax_scale: float = 0.0, imp_out=None, workspace=None, stream=None) -> torch.Tensor:
+    p = kv_params(Q, K, 1, 0.5, 1, softmax_scale)
+    H, Lk, _ = K.shape
+    if imp_out is None:
+        imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
+    _check("fc_kv_importance", _lib.fc_kv_importance(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(imp_out), _ptr(ws),
+                                                     ws.numel(), _stream(stream)))
+    return imp_out
+
+
+def fc_kv_redundancy(K, r_out=None, workspace=None, stream=None) -> torch.Tensor:
+    H, Lk, d = K.shape
+    p = fc_kv_params(H, d, 1, Lk, 1, 0.5, 1, 0.0, _dtype_code(K))
+    if r_out is None:
+        r_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
+    _check("fc_kv_redundancy", _lib.fc_kv_redundancy(ctypes.byref(p), _ptr(K), _ptr(r_out), _ptr(ws), ws.numel(),
+                                                     _stream(stream)))
+    return r_out
+
+
+def fc_kv_select(imp, r, B_budget: int, lam: float, pool_window: int, K=None, V=None, want_scores: bool = True,
+                 workspace=None, stream=None) -> Dict[str, torch.Tensor]:
+    H, Lk = imp.shape
+    d = K.shape[2] if K is not None else 64
+    dt = _dtype_code(K) if K is not None else FC_F32
+    p = fc_kv_params(H, d, 1, Lk, int(B_budget), float(lam), int(pool_window), 0.0, dt)
+    Bp = min(int(B_budget), Lk)
+    dev = imp.device
+    out = {"idx": torch.empty((H, Bp), dtype=torch.int32, device=dev)}
+    if K is not None:
+        out["K_out"] = torch.empty((H, Bp, d), dtype=K.dtype, device=dev)
+        out["V_out"] = torch.empty((H, Bp, d), dtype=V.dtype, device=dev)
+    if want_scores:
+        for k in ("score", "imp_pooled", "red"):
+            out[k] = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), dev, workspace)
+    _check("fc_kv_select", _lib.fc_kv_select(
+        ctypes.byref(p), _ptr(imp), _ptr(r), _ptr(K), _ptr(V), _ptr(out.get("K_out")), _ptr(out.get("V_out")),
+        _ptr(out["idx"]), _ptr(out.get("score")), _ptr(out.get("imp_pooled")), _ptr(out.get("red")),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def fc_topb_select_workspace_bytes(H: int, L: int) -> int:
+    return int(_lib.fc_topb_select_workspace_bytes(int(H), int(L)))
+
+
+def fc_topb_select(scores: torch.Tensor, B: int, idx_out=None, workspace=None, stream=None) -> torch.Tensor:
+    H, L = scores.shape
+    if idx_out is None:
+        idx_out = torch.empty((H, min(int(B), L)), dtype=torch.int32, device=scores.device)
+    ws = _workspace(fc_topb_select_workspace_bytes(H, L), scores.device, workspace)
+    _check("fc_topb_select", _lib.fc_topb_select(H, L, int(B), _ptr(scores), _ptr(idx_out), _ptr(ws), ws.numel(),
+                                                 _stream(stream)))
+    return idx_out
+
+
+def _offsets(chunk_offsets: Sequence[int]):
+    arr = (ctypes.c_int64 * len(chunk_offsets))(*[int(x) for x in chunk_offsets])
+    return arr
+
+
+def fc_chunk_rel_l1_workspace_bytes(p: fc_l1_params, chunk_offsets: Sequence[int]) -> int:
+    return int(_lib.fc_chunk_rel_l1_workspace_bytes(ctypes.byref(p), _offsets(chunk_offsets)))
+
+
+def fc_chunk_rel_l1_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check("fc_chunk_rel_l1_workspace_init",
+           _lib.fc_chunk_rel_l1_workspace_init(_ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+class ChunkDecider:
+    """Holds the per-chunk state (step, f) and the workspace on the device and
+    calls fc_chunk_rel_l1_decide once per denoising step."""
+
+    def __init__(self, chunk_offsets: Sequence[int], m: int, eps: float, dtype: torch.dtype, device="cuda"):
+        self.offsets = [int(x) for x in chunk_offsets]
+        n = len(self.offsets) - 1
+        self.p = fc_l1_params(n, int(m), float(eps), FC_BF16 if dtype == torch.bfloat16 else FC_F32)
+        nbytes = fc_chunk_rel_l1_workspace_bytes(self.p, self.offsets)
+        if nbytes == 0:
+            raise FlowCacheError("fc_chunk_rel_l1_workspace_bytes", FC_ERR_INVALID_ARG)
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.step = torch.full((n,), -1, dtype=torch.int32, device=device)
+        self.f = torch.zeros(n, dtype=torch.float32, device=device)
+        self.recompute = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.l1 = torch.zeros(n, dtype=torch.float32, device=device)
+
+    def decide(self, X_t: torch.Tensor, X_tm1: torch.Tensor, stream=None) -> None:
+        fc_chunk_rel_l1_decide(self.p, self.offsets, X_t, X_tm1, self.step, self.f, self.recompute, self.l1,
+                               self.workspace, stream)
+
+
+def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, step, f, recompute,
+                           l1_rel_out=None, workspace=None, stream=None) -> None:
+    _check("fc_chunk_rel_l1_decide", _lib.fc_chunk_rel_l1_decide(
+        ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
+        _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))

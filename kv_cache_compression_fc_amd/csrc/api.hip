@@ -1,0 +1,281 @@
+// C ABI of libflowcache: argument checks, workspace layout and the launch
+// sequence of each entry point.  Declarations and the contract live in
+// include/flowcache.h.
+#include <math.h>
+
+#include "../../include/flowcache.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace fc;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- KV compression -------------------------------------------------------------------
+struct KvLayout {
+    ImpPlan plan;
+    int nbu, nbr, nbs;
+    size_t part, imp, r, u_part, red_part, keys, hist, counts, state, total;
+};
+
+fc_status check_kv(const fc_kv_params* p) {
+    if (p == nullptr) return FC_ERR_INVALID_ARG;
+    if (p->H < 1 || p->d < 1 || p->L_q < 1 || p->L_k < 1 || p->B_budget < 1) return FC_ERR_INVALID_ARG;
+    if (!(p->lambda >= 0.0f && p->lambda <= 1.0f)) return FC_ERR_INVALID_ARG;
+    if (p->pool_window < 1 || p->pool_window % 2 == 0 || p->pool_window > 129) return FC_ERR_INVALID_ARG;
+    if (!(p->softmax_scale >= 0.0f) || isinf(p->softmax_scale)) return FC_ERR_INVALID_ARG;
+    if (p->dtype != FC_F32 && p->dtype != FC_BF16) return FC_ERR_UNSUPPORTED;
+    if (p->d != 64 && p->d != 128) return FC_ERR_UNSUPPORTED;
+    if (p->H > 65535) return FC_ERR_UNSUPPORTED;
+    return FC_OK;
+}
+
+KvLayout kv_layout(const fc_kv_params* p) {
+    KvLayout L{};
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    L.plan = imp_plan(p->H, p->L_q, p->L_k, dt);
+    L.nbu = red_nbu(p->L_k);
+    L.nbr = red_nbr(p->L_k);
+    L.nbs = sel_nblk(p->L_k);
+    const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
+    size_t o = 0;
+    L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
+    L.imp = o;      o = align_up(o + H * Lk * sizeof(float));
+    L.r = o;        o = align_up(o + H * Lk * sizeof(float));
+    L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
+    L.red_part = o; o = align_up(o + H * L.nbr * sizeof(float2));
+    L.keys = o;     o = align_up(o + H * Lk * sizeof(uint32_t));
+    L.hist = o;     o = align_up(o + H * kHistWordsPerHead * sizeof(uint32_t));
+    L.counts = o;   o = align_up(o + H * L.nbs * 2 * sizeof(uint32_t));
+    L.state = o;    o = align_up(o + H * 2 * sizeof(uint32_t));
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+SelBuffers sel_buffers(void* ws, const KvLayout& L) {
+    return SelBuffers{at<uint32_t>(ws, L.keys), at<uint32_t>(ws, L.hist), at<uint32_t>(ws, L.counts),
+                      at<uint32_t>(ws, L.state)};
+}
+
+float log2_scale(const fc_kv_params* p) {
+    const float scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->d);
+    return scale * kLog2e;
+}
+
+fc_status hip_status(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_HIP; }
+
+#define FC_TRY(expr)                                 \
+    do {                                             \
+        hipError_t e_ = (expr);                      \
+        if (e_ != hipSuccess) return FC_ERR_HIP;     \
+    } while (0)
+
+fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp,
+                         void* ws, hipStream_t s) {
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    const float c = log2_scale(p);
+    float2* part = at<float2>(ws, L.part);
+    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, part, imp, p->H, p->L_q, p->L_k, L.plan.nsplit, c, s));
+    return FC_OK;
+}
+
+// ---- chunk L1 ------------------------------------------------------------------------------
+fc_status chunk_table(const fc_l1_params* p, const int64_t* off, ChunkTable* tab) {
+    if (p == nullptr || off == nullptr) return FC_ERR_INVALID_ARG;
+    if (p->n_chunks < 1) return FC_ERR_INVALID_ARG;
+    if (p->n_chunks > FC_MAX_CHUNKS || p->n_chunks > kMaxChunks) return FC_ERR_UNSUPPORTED;
+    if (p->dtype != FC_F32 && p->dtype != FC_BF16) return FC_ERR_UNSUPPORTED;
+    if (p->m < 0 || !(p->eps >= 0.0f)) return FC_ERR_INVALID_ARG;
+    if (off[0] < 0) return FC_ERR_INVALID_ARG;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    tab->n = p->n_chunks;
+    long long blocks = 0;
+    for (int i = 0; i < p->n_chunks; ++i) {
+        if (off[i + 1] < off[i]) return FC_ERR_INVALID_ARG;
+        tab->off[i] = off[i];
+        tab->blk_start[i] = (int32_t)blocks;
+        blocks += chunk_blocks_for(off[i + 1] - off[i], dt);
+        if (blocks > 0x7fffffffLL) return FC_ERR_UNSUPPORTED;
+    }
+    tab->off[p->n_chunks] = off[p->n_chunks];
+    tab->blk_start[p->n_chunks] = (int32_t)blocks;
+    return FC_OK;
+}
+
+size_t chunk_ws_bytes(const ChunkTable& tab, size_t* partial_off) {
+    const size_t counters = align_up((size_t)tab.n * sizeof(uint32_t));
+    *partial_off = counters;
+    return counters + align_up((size_t)tab.blk_start[tab.n] * sizeof(float2));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fc_status_string(fc_status s) {
+    switch (s) {
+        case FC_OK: return "ok";
+        case FC_ERR_INVALID_ARG: return "invalid argument";
+        case FC_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FC_ERR_WORKSPACE: return "workspace missing or too small";
+        case FC_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p) {
+    if (check_kv(p) != FC_OK) return 0;
+    return kv_layout(p).total;
+}
+
+fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, const void* V, void* K_out,
+                         void* V_out, int32_t* idx_out, float* score_out, float* imp_pooled_out, float* red_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!Q || !K || !V || !K_out || !V_out || !idx_out) return FC_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
+        return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
+    void* ws = workspace;
+    float* imp = at<float>(ws, L.imp);
+    float* r = at<float>(ws, L.r);
+    float2* red_part = at<float2>(ws, L.red_part);
+    const SelBuffers sb = sel_buffers(ws, L);
+    // redundancy (also clears the selection histograms)
+    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, sb.hist, kHistWordsPerHead, s));
+    FC_TRY(launch_red_dot(dt, p->d, K, at<float>(ws, L.u_part), r, red_part, p->H, p->L_k, s));
+    // importance
+    st = run_importance(p, L, Q, K, imp, ws, s);
+    if (st != FC_OK) return st;
+    // pool + score + top-B + gather
+    FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
+                                    red_out, sb, p->H, p->L_k, s));
+    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, dt, p->d, K, V, K_out, V_out, idx_out, s));
+    return FC_OK;
+}
+
+fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, float* imp_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!Q || !K || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!K || !r_out || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(workspace, L.u_part), p->H, p->L_k, nullptr, 0, s));
+    FC_TRY(launch_red_dot(dt, p->d, K, at<float>(workspace, L.u_part), r_out, at<float2>(workspace, L.red_part),
+                          p->H, p->L_k, s));
+    return FC_OK;
+}
+
+fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, const void* K, const void* V,
+                       void* K_out, void* V_out, int32_t* idx_out, float* score_out, float* imp_pooled_out,
+                       float* red_out, void* workspace, size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!imp || !r || !idx_out) return FC_ERR_INVALID_ARG;
+    const bool gather = K || V || K_out || V_out;
+    if (gather && !(K && V && K_out && V_out)) return FC_ERR_INVALID_ARG;
+    if (gather && (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out)))
+        return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
+    const SelBuffers sb = sel_buffers(workspace, L);
+    float2* red_part = at<float2>(workspace, L.red_part);
+    FC_TRY(launch_red_stats(r, red_part, p->H, p->L_k, sb.hist, kHistWordsPerHead, s));
+    FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
+                                    red_out, sb, p->H, p->L_k, s));
+    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, dt, p->d, gather ? K : nullptr, V, K_out, V_out, idx_out, s));
+    return FC_OK;
+}
+
+size_t fc_topb_select_workspace_bytes(int32_t H, int32_t L) {
+    if (H < 1 || L < 1 || H > 65535) return 0;
+    const size_t h = (size_t)H;
+    size_t o = align_up(h * (size_t)L * sizeof(uint32_t));             // keys
+    o += align_up(h * kHistWordsPerHead * sizeof(uint32_t));            // hist
+    o += align_up(h * sel_nblk(L) * 2 * sizeof(uint32_t));              // counts
+    o += align_up(h * 2 * sizeof(uint32_t));                            // state
+    return o;
+}
+
+fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, int32_t* idx_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (H < 1 || L < 1 || B < 1 || !scores || !idx_out) return FC_ERR_INVALID_ARG;
+    if (H > 65535) return FC_ERR_UNSUPPORTED;
+    const size_t need = fc_topb_select_workspace_bytes(H, L);
+    if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t h = (size_t)H;
+    size_t o = 0;
+    SelBuffers sb;
+    sb.keys = at<uint32_t>(workspace, o);   o += align_up(h * (size_t)L * sizeof(uint32_t));
+    sb.hist = at<uint32_t>(workspace, o);   o += align_up(h * kHistWordsPerHead * sizeof(uint32_t));
+    sb.counts = at<uint32_t>(workspace, o); o += align_up(h * sel_nblk(L) * 2 * sizeof(uint32_t));
+    sb.state = at<uint32_t>(workspace, o);
+    const int Bp = B < L ? B : L;
+    FC_TRY(launch_zero_u32(sb.hist, h * kHistWordsPerHead, s));
+    FC_TRY(launch_sel_keys_from_scores(scores, sb, H, L, s));
+    FC_TRY(launch_sel_finish(sb, H, L, Bp, kF32, 64, nullptr, nullptr, nullptr, nullptr, idx_out, s));
+    return FC_OK;
+}
+
+size_t fc_chunk_rel_l1_workspace_bytes(const fc_l1_params* p, const int64_t* chunk_offsets) {
+    ChunkTable tab;
+    if (chunk_table(p, chunk_offsets, &tab) != FC_OK) return 0;
+    size_t po;
+    return chunk_ws_bytes(tab, &po);
+}
+
+fc_status fc_chunk_rel_l1_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace == nullptr || workspace_bytes % 4 != 0) return FC_ERR_INVALID_ARG;
+    return hip_status(launch_zero_u32(static_cast<uint32_t*>(workspace), workspace_bytes / 4,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,
+                                 const void* X_tm1, int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    ChunkTable tab;
+    fc_status st = chunk_table(p, chunk_offsets, &tab);
+    if (st != FC_OK) return st;
+    if (!X_t || !X_tm1 || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
+    if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
+    size_t po;
+    const size_t need = chunk_ws_bytes(tab, &po);
+    if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, step, f, recompute, l1_rel_out,
+                                      at<float2>(workspace, po), static_cast<uint32_t*>(workspace), p->m, p->eps,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

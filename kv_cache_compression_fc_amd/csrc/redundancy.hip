@@ -1,0 +1,223 @@
+// Redundancy of the clean keys, "Flow Caching for Autoregressive Video
+// Generation" (papernotes digest), Key designs item 3: the cosine similarity
+// of l2-normalised keys with the diagonal zeroed, averaged over tokens, then
+// softmaxed.  With khat_j = k_j / max(||k_j||, 1e-12) and u = sum_i khat_i,
+//     r_j = (1/L_k) sum_{i != j} khat_i . khat_j = (u . khat_j - khat_j . khat_j) / L_k,
+// so no L_k x L_k matrix is formed.  Two streaming passes over K, both
+// HBM-bound (16-byte loads, one row per TPR lanes, wave reductions):
+//   pass A: per-block partial u (fixed-order reduction, no float atomics);
+//   pass B: u from the partials, r_j, and per-block (max, sum e^{r-max}) for
+//           the softmax over j.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fc {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Thread layout for one row of D elements of type DT: 16 bytes per lane.
+template <int DT, int D>
+struct RowLayout {
+    static constexpr int kVec = 16 / Elem<DT>::kBytes;  // elements per lane
+    static constexpr int kTpr = D / kVec;                // lanes per row
+    static constexpr int kRpi = kThreads / kTpr;         // rows per block step
+    static_assert(kTpr <= kWave && kWave % kTpr == 0, "a row must fit in one wave");
+};
+
+template <int DT>
+__device__ __forceinline__ void load_vec(const void* p, float* x);
+template <>
+__device__ __forceinline__ void load_vec<kBF16>(const void* p, float* x) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load_vec<kF32>(const void* p, float* x) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
+__device__ __forceinline__ void zero_slice(uint32_t* hist, size_t words, int blk, int nblk) {
+    if (hist == nullptr) return;
+    const size_t per = (words + nblk - 1) / nblk;
+    const size_t b = (size_t)blk * per;
+    const size_t e = b + per < words ? b + per : words;
+    for (size_t i = b + threadIdx.x; i < e; i += kThreads) hist[i] = 0u;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void red_norm_sum_kernel(const void* __restrict__ K,
+                                                                float* __restrict__ u_part, int Lk,
+                                                                uint32_t* __restrict__ hist,
+                                                                size_t hist_words) {
+    using RL = RowLayout<DT, D>;
+    constexpr int kE = Elem<DT>::kBytes;
+    __shared__ float red[RL::kRpi][D];
+    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    zero_slice(hist ? hist + (size_t)h * hist_words : nullptr, hist_words, blk, nblk);
+
+    const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
+    const int rows = (Lk + nblk - 1) / nblk;
+    const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
+    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
+    float u[RL::kVec];
+#pragma unroll
+    for (int v = 0; v < RL::kVec; ++v) u[v] = 0.f;
+    for (int row = r0 + g; row < r1; row += RL::kRpi) {
+        float x[RL::kVec];
+        load_vec<DT>(Kh + ((size_t)row * D + e * RL::kVec) * kE, x);
+        float n2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < RL::kVec; ++v) n2 = fmaf(x[v], x[v], n2);
+        n2 = group_sum<RL::kTpr>(n2);
+        const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+#pragma unroll
+        for (int v = 0; v < RL::kVec; ++v) u[v] = fmaf(x[v], inv, u[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < RL::kVec; ++v) red[g][e * RL::kVec + v] = u[v];
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += kThreads) {
+        float acc = 0.f;
+        for (int i = 0; i < RL::kRpi; ++i) acc += red[i][c];
+        u_part[((size_t)h * nblk + blk) * D + c] = acc;
+    }
+}
+
+// Online softmax statistics of a block's values, merged over the block.
+// Each thread passes its running (m, s) with s = sum e^{x - m}; the result is
+// written by thread 0.
+__device__ __forceinline__ void block_softmax_stats(float m, float s, float2* out) {
+    __shared__ float sm[kThreads / kWave], ss[kThreads / kWave];
+    // natural-log statistics are kept in base 2 inside: x*log2e
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+        lse2_merge(m, s, m2, s2);
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) { sm[wave] = m; ss[wave] = s; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = sm[0], S = ss[0];
+        for (int w = 1; w < kThreads / kWave; ++w) lse2_merge(M, S, sm[w], ss[w]);
+        *out = make_float2(M, S);
+    }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restrict__ K,
+                                                           const float* __restrict__ u_part, int nbu,
+                                                           float* __restrict__ r, float2* __restrict__ red_part,
+                                                           int Lk) {
+    using RL = RowLayout<DT, D>;
+    constexpr int kE = Elem<DT>::kBytes;
+    __shared__ float ush[D];
+    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    for (int c = threadIdx.x; c < D; c += kThreads) {
+        float acc = 0.f;
+        for (int i = 0; i < nbu; ++i) acc += u_part[((size_t)h * nbu + i) * D + c];
+        ush[c] = acc;
+    }
+    __syncthreads();
+    const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
+    float u[RL::kVec];
+#pragma unroll
+    for (int v = 0; v < RL::kVec; ++v) u[v] = ush[e * RL::kVec + v];
+
+    const int rows = (Lk + nblk - 1) / nblk;
+    const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
+    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
+    const float inv_lk = 1.0f / (float)Lk;
+    float m = -1e30f, s = 0.f;  // base-2 running stats of r * log2e
+    for (int row = r0 + g; row < r1; row += RL::kRpi) {
+        float x[RL::kVec];
+        load_vec<DT>(Kh + ((size_t)row * D + e * RL::kVec) * kE, x);
+        float dot = 0.f, n2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < RL::kVec; ++v) {
+            dot = fmaf(x[v], u[v], dot);
+            n2 = fmaf(x[v], x[v], n2);
+        }
+        dot = group_sum<RL::kTpr>(dot);
+        n2 = group_sum<RL::kTpr>(n2);
+        const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+        const float rj = (dot * inv - n2 * inv * inv) * inv_lk;
+        if (e == 0) {
+            r[(size_t)h * Lk + row] = rj;
+            lse2_merge(m, s, rj * kLog2e, 1.0f);
+        }
+    }
+    block_softmax_stats(m, s, red_part + (size_t)h * nblk + blk);
+}
+
+__global__ __launch_bounds__(kThreads) void red_stats_kernel(const float* __restrict__ r,
+                                                             float2* __restrict__ red_part, int Lk,
+                                                             uint32_t* __restrict__ hist,
+                                                             size_t hist_words) {
+    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    zero_slice(hist ? hist + (size_t)h * hist_words : nullptr, hist_words, blk, nblk);
+    const int rows = (Lk + nblk - 1) / nblk;
+    const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
+    float m = -1e30f, s = 0.f;
+    for (int j = r0 + threadIdx.x; j < r1; j += kThreads) lse2_merge(m, s, r[(size_t)h * Lk + j] * kLog2e, 1.0f);
+    block_softmax_stats(m, s, red_part + (size_t)h * nblk + blk);
+}
+
+template <int DT, int D>
+hipError_t norm_sum_launch(const void* K, float* u_part, int H, int Lk, uint32_t* hist, size_t hist_words,
+                           hipStream_t s) {
+    hipLaunchKernelGGL((red_norm_sum_kernel<DT, D>), dim3(red_nbu(Lk), H), dim3(kThreads), 0, s, K, u_part,
+                       Lk, hist, hist_words);
+    return hipGetLastError();
+}
+template <int DT, int D>
+hipError_t dot_launch(const void* K, const float* u_part, float* r, float2* red_part, int H, int Lk,
+                      hipStream_t s) {
+    hipLaunchKernelGGL((red_dot_kernel<DT, D>), dim3(red_nbr(Lk), H), dim3(kThreads), 0, s, K, u_part,
+                       red_nbu(Lk), r, red_part, Lk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int red_nbu(int Lk) {
+    int n = (Lk + 511) / 512;
+    return n < 1 ? 1 : (n > 64 ? 64 : n);
+}
+int red_nbr(int Lk) {
+    int n = (Lk + 127) / 128;
+    return n < 1 ? 1 : (n > 128 ? 128 : n);
+}
+
+hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, uint32_t* hist,
+                               size_t hist_words, hipStream_t s) {
+    if (dt == kBF16) return d == 128 ? norm_sum_launch<kBF16, 128>(K, u_part, H, Lk, hist, hist_words, s)
+                                     : norm_sum_launch<kBF16, 64>(K, u_part, H, Lk, hist, hist_words, s);
+    return d == 128 ? norm_sum_launch<kF32, 128>(K, u_part, H, Lk, hist, hist_words, s)
+                    : norm_sum_launch<kF32, 64>(K, u_part, H, Lk, hist, hist_words, s);
+}
+
+hipError_t launch_red_dot(int dt, int d, const void* K, const float* u_part, float* r, float2* red_part,
+                          int H, int Lk, hipStream_t s) {
+    if (dt == kBF16) return d == 128 ? dot_launch<kBF16, 128>(K, u_part, r, red_part, H, Lk, s)
+                                     : dot_launch<kBF16, 64>(K, u_part, r, red_part, H, Lk, s);
+    return d == 128 ? dot_launch<kF32, 128>(K, u_part, r, red_part, H, Lk, s)
+                    : dot_launch<kF32, 64>(K, u_part, r, red_part, H, Lk, s);
+}
+
+hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, uint32_t* hist, size_t hist_words,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(red_stats_kernel, dim3(red_nbr(Lk), H), dim3(kThreads), 0, s, r, red_part, Lk, hist,
+                       hist_words);
+    return hipGetLastError();
+}
+
+}  // namespace fc

@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol include/flowcache.h declares,
+and rejects bad arguments on the host (no GPU work is queued on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flowcache.h")
+LIB = os.path.join(ROOT, "kv_cache_compression_fc_amd", "libflowcache.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return sorted(set(re.findall(r"\b(fc_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not os.path.exists(LIB):
+        pytest.fail("libflowcache.so is not built (run __graft_entry__.build())")
+    from kv_cache_compression_fc_amd import binding
+    return binding
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for want in ("fc_kv_compress", "fc_chunk_rel_l1_decide", "fc_kv_compress_workspace_bytes",
+                 "fc_chunk_rel_l1_workspace_bytes", "fc_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(fc):
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(fc.EXPORTS) == set(names)
+
+
+def test_status_strings(fc):
+    assert fc.fc_status_string(fc.FC_OK) == "ok"
+    assert "workspace" in fc.fc_status_string(fc.FC_ERR_WORKSPACE)
+    assert fc.fc_status_string(99) == "unknown status"
+
+
+def _params(fc, **kw):
+    base = dict(H=24, d=128, L_q=3600, L_k=18000, B_budget=7200, lambda_=0.5, pool_window=7, softmax_scale=0.0,
+                dtype=fc.FC_BF16)
+    base.update(kw)
+    return fc.fc_kv_params(**base)
+
+
+def test_kv_workspace_query(fc):
+    n = fc.fc_kv_compress_workspace_bytes(_params(fc))
+    # at least imp, r and keys (3 x 4 B per key-head) plus the lse partials
+    assert n >= 3 * 4 * 24 * 18000 + 8 * 24 * 3600
+    assert n % 256 == 0
+    for bad in (dict(H=0), dict(L_k=0), dict(B_budget=0), dict(lambda_=1.5), dict(lambda_=float("nan")),
+                dict(pool_window=4), dict(pool_window=0), dict(softmax_scale=-1.0), dict(d=96), dict(dtype=7)):
+        assert fc.fc_kv_compress_workspace_bytes(_params(fc, **bad)) == 0, bad
+
+
+def test_kv_argument_errors(fc):
+    lib = fc._lib
+    p = _params(fc)
+    dummy = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(4096)
+    need = fc.fc_kv_compress_workspace_bytes(p)
+    # null required pointer
+    st = lib.fc_kv_compress(ctypes.byref(p), None, dummy, dummy, dummy, dummy, dummy, None, None, None, ws, need, None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    # misaligned tensor
+    st = lib.fc_kv_compress(ctypes.byref(p), ctypes.c_void_p(4098), dummy, dummy, dummy, dummy, dummy, None, None,
+                            None, ws, need, None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    # short workspace
+    st = lib.fc_kv_compress(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, None, None, None, ws,
+                            need - 1, None)
+    assert st == fc.FC_ERR_WORKSPACE
+    # unsupported head dim / dtype
+    st = lib.fc_kv_compress(ctypes.byref(_params(fc, d=96)), dummy, dummy, dummy, dummy, dummy, dummy, None, None,
+                            None, ws, need, None)
+    assert st == fc.FC_ERR_UNSUPPORTED
+    st = lib.fc_kv_compress(ctypes.byref(_params(fc, pool_window=8)), dummy, dummy, dummy, dummy, dummy, dummy,
+                            None, None, None, ws, need, None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    # select: partial gather pointers
+    st = lib.fc_kv_select(ctypes.byref(p), dummy, dummy, dummy, None, None, None, dummy, None, None, None, ws, need,
+                          None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    assert lib.fc_topb_select(2, 10, 0, dummy, dummy, ws, 1 << 20, None) == fc.FC_ERR_INVALID_ARG
+    assert lib.fc_topb_select(2, 10, 3, dummy, dummy, ws, 16, None) == fc.FC_ERR_WORKSPACE
+
+
+def test_chunk_workspace_and_errors(fc):
+    lib = fc._lib
+    p = fc.fc_l1_params(16, 5, 0.01, fc.FC_BF16)
+    e = 64 * 8 * 90 * 160
+    offs = [i * e for i in range(17)]
+    n = fc.fc_chunk_rel_l1_workspace_bytes(p, offs)
+    assert n > 16 * 4
+    assert fc.fc_chunk_rel_l1_workspace_bytes(fc.fc_l1_params(0, 5, 0.01, fc.FC_BF16), [0]) == 0
+    assert fc.fc_chunk_rel_l1_workspace_bytes(fc.fc_l1_params(2, 5, 0.01, fc.FC_BF16), [0, 5, 3]) == 0
+    assert fc.fc_chunk_rel_l1_workspace_bytes(fc.fc_l1_params(2, -1, 0.01, fc.FC_BF16), [0, 5, 9]) == 0
+    assert fc.fc_chunk_rel_l1_workspace_bytes(fc.fc_l1_params(2, 1, float("nan"), fc.FC_BF16), [0, 5, 9]) == 0
+    assert fc.fc_chunk_rel_l1_workspace_bytes(fc.fc_l1_params(200, 1, 0.1, fc.FC_BF16), list(range(201))) == 0
+    dummy = ctypes.c_void_p(4096)
+    arr = fc._offsets(offs)
+    st = lib.fc_chunk_rel_l1_decide(ctypes.byref(p), arr, dummy, dummy, dummy, dummy, None, None, dummy, n, None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    st = lib.fc_chunk_rel_l1_decide(ctypes.byref(p), arr, dummy, dummy, dummy, dummy, dummy, None, dummy, n - 1,
+                                    None)
+    assert st == fc.FC_ERR_WORKSPACE
+    st = lib.fc_chunk_rel_l1_decide(ctypes.byref(p), arr, ctypes.c_void_p(4100), dummy, dummy, dummy, dummy, None,
+                                    dummy, n, None)
+    assert st == fc.FC_ERR_INVALID_ARG

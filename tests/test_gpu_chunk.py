@@ -1,0 +1,167 @@
+"""GPU parity of fc_chunk_rel_l1_decide against the fp64 oracle, in lockstep
+over whole synthetic trajectories, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_fc_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+L1_RTOL = 1e-5       # float32 slab sums vs fp64 (reported value only)
+EPS_BAND = 1e-6      # decisions within this distance of eps are exempt
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from kv_cache_compression_fc_amd import binding
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+class Lockstep:
+    """Oracle state per chunk, advanced beside the GPU's."""
+
+    def __init__(self, n, m, eps):
+        self.f = np.zeros(n)
+        self.m, self.eps = m, eps
+        self.exempt = 0
+        self.decisions = 0
+
+    def step(self, steps, l1_ref, rec_gpu, f_gpu, l1_gpu):
+        for i, n in enumerate(steps):
+            if n < 0:
+                continue
+            f_prev = self.f[i]
+            r, f_new = oracle.decide(n, f_prev, l1_ref[i], self.m, self.eps)
+            if np.isfinite(l1_ref[i]):
+                assert abs(l1_gpu[i] - l1_ref[i]) <= L1_RTOL * l1_ref[i] + 1e-12, (i, n, l1_gpu[i], l1_ref[i])
+            else:
+                assert l1_gpu[i] == np.inf
+            exempt = n >= self.m and abs(f_prev + l1_ref[i] - self.eps) <= EPS_BAND
+            self.decisions += 1
+            if exempt:
+                self.exempt += 1
+            else:
+                assert bool(rec_gpu[i]) == r, f"chunk {i} local step {n}: gpu {rec_gpu[i]} oracle {r}"
+                assert abs(f_gpu[i] - f_new) <= 1e-6, (i, n, f_gpu[i], f_new)
+            self.f[i] = f_new if bool(rec_gpu[i]) == r else float(f_gpu[i])
+
+
+def run_trajectory(fc, cfg, eps_list, g_steps=None, seed=0):
+    tr = synth.ChunkTrajectory(cfg, seed=seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    decs = [fc.ChunkDecider(tr.offsets, cfg.m, e, dt, DEV) for e in eps_list]
+    locks = [Lockstep(cfg.n_chunks, cfg.m, e) for e in eps_list]
+    g_steps = range(tr.n_global_steps()) if g_steps is None else g_steps
+    for g in g_steps:
+        xt, xtm1, steps = tr.pair(g)
+        st = torch.tensor(steps, dtype=torch.int32)
+        xt_d, xtm1_d = xt.to(DEV), xtm1.to(DEV)
+        l1_ref = oracle.chunk_l1_rel(xt, xtm1, tr.offsets)
+        for dec, lk in zip(decs, locks):
+            # chunks that start now enter at local step 0; finished ones leave (-1)
+            cur = dec.step.cpu()
+            new = torch.where(st < 0, torch.full_like(st, -1), torch.where(cur < 0, torch.zeros_like(st), cur))
+            assert torch.equal(new[st >= 0], st[st >= 0]), "device step counters drifted"
+            dec.step.copy_(new.to(DEV))
+            dec.decide(xt_d, xtm1_d)
+            torch.cuda.synchronize()
+            lk.step(steps, l1_ref, dec.recompute.cpu().numpy(), dec.f.cpu().numpy(), dec.l1.cpu().numpy())
+    return locks
+
+
+def test_tiny_trajectory(fc):
+    cfg = synth.CHUNK_CONFIGS["tiny"]
+    say("case: tiny chunk trajectory 4 x 256 fp32, 10 steps, m=2, eps=0.01")
+    locks = run_trajectory(fc, cfg, cfg.eps)
+    assert locks[0].decisions == cfg.n_chunks * cfg.N
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_trajectory_other_thresholds(fc, seed):
+    cfg = synth.ChunkConfig("t2", 5, 1000, 30, 3, (0.002, 0.01, 0.05), "f32", 2)
+    say(f"case: 5 chunks x 1000 fp32, staggered, 30 steps, seed {seed}")
+    locks = run_trajectory(fc, cfg, cfg.eps, seed=seed)
+    assert all(lk.decisions == cfg.n_chunks * cfg.N for lk in locks)
+
+
+def test_scale_trajectory_first_steps(fc):
+    # 16 chunks x 7,372,800 bf16, staggered starts; the first 24 global steps
+    # cover every chunk's forced steps and many threshold decisions
+    cfg = synth.CHUNK_CONFIGS["scale"]
+    say("case: 16 chunks x 64x8x90x160 bf16, global steps 0..23, eps 0.01 and 0.015")
+    locks = run_trajectory(fc, cfg, cfg.eps, g_steps=range(24))
+    assert all(lk.decisions > 100 for lk in locks)
+
+
+def test_unaligned_offsets_and_edge_chunks(fc):
+    # offsets not multiples of the vector width, an empty chunk, a zero chunk
+    rng = np.random.default_rng(4)
+    sizes = [1, 7, 0, 33333, 8, 100001, 5]
+    offs = np.concatenate([[3], 3 + np.cumsum(sizes)]).tolist()
+    total = offs[-1] + 2
+    for dtype in (torch.bfloat16, torch.float32):
+        a = torch.from_numpy(rng.standard_normal(total).astype(np.float32)).to(dtype)
+        b = torch.from_numpy(rng.standard_normal(total).astype(np.float32)).to(dtype)
+        a[offs[5]:offs[6]] = 0  # ||X_t||_1 = 0 -> +inf -> recompute
+        say(f"case: unaligned chunk offsets {offs} dtype {dtype}")
+        dec = fc.ChunkDecider(offs, 0, 0.5, dtype, DEV)
+        dec.step.zero_()
+        dec.f.fill_(0.25)
+        dec.decide(a.to(DEV), b.to(DEV))
+        torch.cuda.synchronize()
+        l1 = oracle.chunk_l1_rel(a, b, offs)
+        got = dec.l1.cpu().numpy()
+        for i in range(len(sizes)):
+            if np.isfinite(l1[i]):
+                assert abs(got[i] - l1[i]) <= 1e-5 * l1[i], (i, got[i], l1[i])
+            else:
+                assert got[i] == np.inf
+        want = [oracle.decide(0, 0.25, l1[i], 0, 0.5) for i in range(len(sizes))]
+        assert dec.recompute.cpu().tolist() == [int(w[0]) for w in want]
+        assert dec.step.cpu().tolist() == [1] * len(sizes)
+
+
+def test_inactive_chunks_untouched(fc):
+    n, e = 6, 5000
+    offs = [i * e for i in range(n + 1)]
+    x = torch.randn(n * e, dtype=torch.float32)
+    y = x + 0.001 * torch.randn(n * e)
+    dec = fc.ChunkDecider(offs, 1, 0.01, torch.float32, DEV)
+    dec.step.copy_(torch.tensor([-1, 0, -5, 3, -1, 2], dtype=torch.int32))
+    dec.f.copy_(torch.tensor([7.0, 0.0, 8.0, 0.001, 9.0, 0.0]))
+    dec.recompute.fill_(77)
+    dec.l1.fill_(-3.0)
+    say("case: inactive chunks are not touched")
+    dec.decide(x.to(DEV), y.to(DEV))
+    torch.cuda.synchronize()
+    st, f, rec, l1 = dec.step.cpu(), dec.f.cpu(), dec.recompute.cpu(), dec.l1.cpu()
+    for i in (0, 2, 4):
+        assert int(rec[i]) == 77 and float(l1[i]) == -3.0
+    assert st.tolist() == [-1, 1, -5, 4, -1, 3]
+    assert float(f[0]) == 7.0 and float(f[2]) == 8.0 and float(f[4]) == 9.0
+    assert int(rec[1]) == 1  # forced (n=0 < m=1)
+
+
+def test_repeated_calls_rearm_workspace(fc):
+    # the same workspace over many calls: the tickets must re-arm every time
+    n, e = 3, 200000
+    offs = [i * e for i in range(n + 1)]
+    x = torch.randn(n * e).to(torch.bfloat16)
+    y = (x.float() * 1.01).to(torch.bfloat16)
+    dec = fc.ChunkDecider(offs, 0, 1.0, torch.bfloat16, DEV)
+    dec.step.zero_()
+    xd, yd = x.to(DEV), y.to(DEV)
+    ref = oracle.chunk_l1_rel(x, y, offs)
+    say("case: 20 calls on one workspace")
+    for k in range(20):
+        dec.decide(xd, yd)
+    torch.cuda.synchronize()
+    assert dec.step.cpu().tolist() == [20] * n
+    np.testing.assert_allclose(dec.l1.cpu().numpy(), ref, rtol=1e-5)
+    assert torch.count_nonzero(dec.workspace[:4 * n]).item() == 0
