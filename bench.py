@@ -1,0 +1,254 @@
+#!/usr/bin/env python
+"""Benchmark of the FlowCache per-step hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs
+already resident in HBM:
+  * fc_kv_compress on the MAGI-like workload (24 heads, d=128, 3600 denoising
+    queries, 18000 clean keys, keep 7200 per head, lambda 0.5, pool window 7,
+    bf16): importance (two MFMA passes), redundancy, pool + score + top-B,
+    K/V compaction;
+  * fc_chunk_rel_l1_decide on 16 concurrent chunks of 64x8x90x160 bf16
+    latents (steady state, all chunks active at staggered local steps).
+
+Prints one JSON line.  `value` is clean-KV token-heads scored and selected per
+second over whole steps (the chunk decision included).  The dominant kernel
+(importance pass 2) is timed on its own with HIP events on the stream it runs
+on, for the roofline entry; the oracle is timed on the host cores on a bounded
+sample for the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "clean KV tokens scored+selected/sec/head; L1 GB/s; % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "imp_colsum_magi_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_compression_fc_amd", "csrc", "importance.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def time_events(fn, reps: int) -> float:
+    """Average ms per call of fn over reps, HIP events on the current stream."""
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def time_graph(fn, reps: int):
+    """Average ms per call with the calls captured in a HIP graph (no host
+    launch gaps between small kernels); falls back to eager event timing."""
+    import torch
+    try:
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / reps, "graph"
+    except Exception as exc:  # pragma: no cover - capture not available
+        log(f"graph capture failed ({exc}); eager timing")
+        return time_events(fn, reps), "eager"
+
+
+def cpu_baseline(cfg, n_heads: int):
+    """The oracle (never tuned) on n_heads heads of the same workload."""
+    import oracle
+    from kv_cache_compression_fc_amd import synth
+    heads = list(range(n_heads))
+    Q, K, V = synth.kv_inputs(cfg, seed=0, heads=heads)
+    t0 = time.perf_counter()
+    oracle.kv_compress(Q, K, V, cfg.B, cfg.lam[0], cfg.w)
+    dt = time.perf_counter() - t0
+    return {"value": n_heads * cfg.Lk / dt, "unit": "token-heads/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{n_heads} of {cfg.H} heads of the MAGI-like workload at full L_q={cfg.Lq}, L_k={cfg.Lk}: "
+                      "importance, redundancy, pool, score, top-B and gather in fp64 (C + OpenMP, numpy)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--cpu-heads", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "the path shards by head with no exchange, so run one process per GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+    from kv_cache_compression_fc_amd import binding as fc
+    from kv_cache_compression_fc_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 3}), flush=True)
+        return 0
+
+    cfg = synth.KV_CONFIGS["magi"]
+    ccfg = synth.CHUNK_CONFIGS["scale"]
+    log(f"generating inputs: {cfg.name} KV workload and {ccfg.n_chunks} chunk states")
+    Q, K, V = synth.kv_inputs(cfg, seed=0)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    del Q, K, V
+    tr = synth.ChunkTrajectory(ccfg, seed=0)
+    g_steady = ccfg.n_chunks - 1  # every chunk active, local steps 15..0
+    xt, xtm1, steps = tr.pair(g_steady)
+    xt_d, xtm1_d = xt.to(dev), xtm1.to(dev)
+    del xt, xtm1, tr
+    dec = fc.ChunkDecider([i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)], ccfg.m, ccfg.eps[0],
+                          torch.bfloat16, dev)
+    dec.step.copy_(torch.tensor(steps, dtype=torch.int32))
+
+    H, Lq, Lk, d, B = cfg.H, cfg.Lq, cfg.Lk, cfg.d, cfg.B
+    Bp = min(B, Lk)
+    p = fc.kv_params(Qd, Kd, B, cfg.lam[0], cfg.w)
+    ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    out = {"K_out": torch.empty((H, Bp, d), dtype=Kd.dtype, device=dev),
+           "V_out": torch.empty((H, Bp, d), dtype=Vd.dtype, device=dev),
+           "idx": torch.empty((H, Bp), dtype=torch.int32, device=dev)}
+
+    def step():
+        fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws)
+        dec.decide(xt_d, xtm1_d)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"ms/step {ms_per_step:.4f} (wall {1e3 * wall / args.steps:.4f})")
+
+    # Per-stage timings (same inputs, same stream, HIP events).
+    reps = args.kernel_reps
+    lse = torch.empty((H, Lq), dtype=torch.float32, device=dev)
+    imp = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+    r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+    fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws)
+    t_lse = time_events(lambda: fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws), reps)
+    t_colsum = time_events(lambda: fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp), reps)
+    t_red, how_red = time_graph(lambda: fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws), reps)
+    t_sel, how_sel = time_graph(lambda: fc.fc_kv_select(imp, r, B, cfg.lam[0], cfg.w, Kd, Vd, want_scores=False,
+                                                        workspace=ws), reps)
+    t_compress = time_events(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws),
+                             reps)
+    t_l1 = time_events(lambda: dec.decide(xt_d, xtm1_d), reps)
+    torch.cuda.synchronize()
+
+    mfma_flops = 2.0 * H * Lq * Lk * d            # one Q K^T product (each pass executes one)
+    red_bytes = H * Lk * (d * 2 + 4)              # read K once, write r
+    sel_bytes = 8 * H * Lk + 4 * H * Bp + 2 * 2 * H * Bp * d * 2   # imp + r, idx, K/V rows read + written
+    l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
+    colsum_tflops = mfma_flops / (t_colsum * 1e-3) / 1e12
+    stages = {
+        "importance_lse_ms": t_lse, "importance_lse_tflops": mfma_flops / (t_lse * 1e-3) / 1e12,
+        "importance_colsum_ms": t_colsum, "importance_colsum_tflops": colsum_tflops,
+        "redundancy_ms": t_red, "redundancy_gbps": red_bytes / (t_red * 1e-3) / 1e9,
+        "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
+        "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
+        "timing": f"events; redundancy {how_red}, select {how_sel}",
+    }
+    for k, v in stages.items():
+        log(f"  {k}: {v}")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_source_sha256_16") == source_hash(KERNEL_SRC):
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": H * Lk / (ms_per_step * 1e-3),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field keys, N(0,1) queries/values; flow-matching chunk trajectories)",
+        "config": {
+            "workload": "MAGI-like KV compression + chunk relative-L1 decision",
+            "H": H, "d": d, "L_q": Lq, "L_k": Lk, "B_budget": B, "lambda": cfg.lam[0], "pool_window": cfg.w,
+            "chunks": ccfg.n_chunks, "chunk_shape": [64, 8, 90, 160], "m": ccfg.m, "eps": ccfg.eps[0],
+        },
+        "tokens_per_s_per_head": Lk / (ms_per_step * 1e-3),
+        "l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "imp_colsum_kernel<bf16,128> (importance pass 2)",
+            "bound": "mfma", "achieved": colsum_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": colsum_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "avg_launch_ms": t_colsum, "algorithmic_per_launch": mfma_flops,
+        },
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

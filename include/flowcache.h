@@ -81,8 +81,9 @@ typedef struct {
     fc_dtype dtype;
 } fc_kv_params;
 
-/* Workspace bytes that fc_kv_compress, fc_kv_importance, fc_kv_redundancy and
- * fc_kv_select need for these parameters (0 if the parameters are invalid). */
+/* Workspace bytes that fc_kv_compress, fc_kv_importance, fc_kv_importance_lse,
+ * fc_kv_redundancy and fc_kv_select need for these parameters (0 if the
+ * parameters are invalid). */
 size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
 
 /*
@@ -117,6 +118,23 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
  */
 fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, float* imp_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_importance_lse -- the first of the two passes alone:
+ *   lse_out[h][i] = log sum_j exp(scale q_i.k_j)   (natural log, f32 [H][L_q])
+ * over the clean keys.  Q, K device (dtype); lse_out device.
+ */
+fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void* K, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_importance_colsum -- the second pass alone, given the normalisers:
+ *   imp_out[h][j] = (1/L_q) sum_i exp(scale q_i.k_j - lse[h][i]).
+ * lse [H][L_q] f32 device (natural log, as written by fc_kv_importance_lse);
+ * one kernel launch, no workspace.
+ */
+fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const void* K, const float* lse,
+                                  float* imp_out, void* stream);
 
 /*
  * fc_kv_redundancy -- mean cosine similarity before its softmax:
@@ -174,10 +192,6 @@ typedef struct {
 /* Workspace bytes for these chunk offsets (host array of n_chunks+1). */
 size_t fc_chunk_rel_l1_workspace_bytes(const fc_l1_params* p, const int64_t* chunk_offsets);
 
-/* Zero a chunk-L1 workspace (device) on `stream`.  Needed once before its
- * first use; every fc_chunk_rel_l1_decide leaves it zeroed again. */
-fc_status fc_chunk_rel_l1_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
-
 /*
  * fc_chunk_rel_l1_decide -- one denoising step's decision for every chunk.
  *   chunk_offsets  host int64[n_chunks+1], element offsets into the states,
@@ -197,7 +211,8 @@ fc_status fc_chunk_rel_l1_workspace_init(void* workspace, size_t workspace_bytes
  *   then step = n + 1.
  * Sums are taken in float32 per thread and combined in a fixed order
  * (deterministic); the decision runs on the device, with no host round trip.
- * The workspace must have been zeroed once (fc_chunk_rel_l1_workspace_init).
+ * The workspace needs no initialisation; calls that share one workspace must
+ * be ordered (same stream).
  */
 fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets,
                                  const void* X_t, const void* X_tm1,

@@ -31,8 +31,9 @@ FC_MAX_CHUNKS = 128
 
 EXPORTS = (
     "fc_status_string", "fc_kv_compress_workspace_bytes", "fc_kv_compress", "fc_kv_importance",
+    "fc_kv_importance_lse", "fc_kv_importance_colsum",
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
-    "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_workspace_init", "fc_chunk_rel_l1_decide",
+    "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
 )
 
 
@@ -58,6 +59,10 @@ _lib.fc_kv_compress.restype = ctypes.c_int
 _lib.fc_kv_compress.argtypes = [ctypes.POINTER(fc_kv_params)] + [_vp] * 9 + [_vp, _sz, _vp]
 _lib.fc_kv_importance.restype = ctypes.c_int
 _lib.fc_kv_importance.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_kv_importance_lse.restype = ctypes.c_int
+_lib.fc_kv_importance_lse.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_kv_importance_colsum.restype = ctypes.c_int
+_lib.fc_kv_importance_colsum.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _vp]
 _lib.fc_kv_redundancy.restype = ctypes.c_int
 _lib.fc_kv_redundancy.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_select.restype = ctypes.c_int
@@ -68,8 +73,6 @@ _lib.fc_topb_select.restype = ctypes.c_int
 _lib.fc_topb_select.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_chunk_rel_l1_workspace_bytes.restype = _sz
 _lib.fc_chunk_rel_l1_workspace_bytes.argtypes = [ctypes.POINTER(fc_l1_params), _i64p]
-_lib.fc_chunk_rel_l1_workspace_init.restype = ctypes.c_int
-_lib.fc_chunk_rel_l1_workspace_init.argtypes = [_vp, _sz, _vp]
 _lib.fc_chunk_rel_l1_decide.restype = ctypes.c_int
 _lib.fc_chunk_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]
@@ -167,6 +170,27 @@ def fc_kv_importance(Q, K, softmax_scale: float = 0.0, imp_out=None, workspace=N
     return imp_out
 
 
+def fc_kv_importance_lse(Q, K, softmax_scale: float = 0.0, lse_out=None, workspace=None, stream=None):
+    p = kv_params(Q, K, 1, 0.5, 1, softmax_scale)
+    H, Lq, _ = Q.shape
+    if lse_out is None:
+        lse_out = torch.empty((H, Lq), dtype=torch.float32, device=Q.device)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
+    _check("fc_kv_importance_lse", _lib.fc_kv_importance_lse(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse_out),
+                                                             _ptr(ws), ws.numel(), _stream(stream)))
+    return lse_out
+
+
+def fc_kv_importance_colsum(Q, K, lse, softmax_scale: float = 0.0, imp_out=None, stream=None):
+    p = kv_params(Q, K, 1, 0.5, 1, softmax_scale)
+    H, Lk, _ = K.shape
+    if imp_out is None:
+        imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    _check("fc_kv_importance_colsum", _lib.fc_kv_importance_colsum(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse),
+                                                                   _ptr(imp_out), _stream(stream)))
+    return imp_out
+
+
 def fc_kv_redundancy(K, r_out=None, workspace=None, stream=None) -> torch.Tensor:
     H, Lk, d = K.shape
     p = fc_kv_params(H, d, 1, Lk, 1, 0.5, 1, 0.0, _dtype_code(K))
@@ -224,11 +248,6 @@ def fc_chunk_rel_l1_workspace_bytes(p: fc_l1_params, chunk_offsets: Sequence[int
     return int(_lib.fc_chunk_rel_l1_workspace_bytes(ctypes.byref(p), _offsets(chunk_offsets)))
 
 
-def fc_chunk_rel_l1_workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    _check("fc_chunk_rel_l1_workspace_init",
-           _lib.fc_chunk_rel_l1_workspace_init(_ptr(workspace), workspace.numel(), _stream(stream)))
-
-
 class ChunkDecider:
     """Holds the per-chunk state (step, f) and the workspace on the device and
     calls fc_chunk_rel_l1_decide once per denoising step."""
@@ -240,7 +259,7 @@ class ChunkDecider:
         nbytes = fc_chunk_rel_l1_workspace_bytes(self.p, self.offsets)
         if nbytes == 0:
             raise FlowCacheError("fc_chunk_rel_l1_workspace_bytes", FC_ERR_INVALID_ARG)
-        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.step = torch.full((n,), -1, dtype=torch.int32, device=device)
         self.f = torch.zeros(n, dtype=torch.float32, device=device)
         self.recompute = torch.zeros(n, dtype=torch.uint8, device=device)

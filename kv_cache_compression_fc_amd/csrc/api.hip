@@ -20,7 +20,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct KvLayout {
     ImpPlan plan;
     int nbu, nbr, nbs;
-    size_t part, imp, r, u_part, red_part, keys, hist, counts, state, total;
+    size_t part, lse, imp, r, u_part, red_part, keys, hist, counts, state, total;
 };
 
 fc_status check_kv(const fc_kv_params* p) {
@@ -45,6 +45,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
+    L.lse = o;      o = align_up(o + H * (size_t)p->L_q * sizeof(float));
     L.imp = o;      o = align_up(o + H * Lk * sizeof(float));
     L.r = o;        o = align_up(o + H * Lk * sizeof(float));
     L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
@@ -83,8 +84,10 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const float c = log2_scale(p);
     float2* part = at<float2>(ws, L.part);
+    float* lse = at<float>(ws, L.lse);
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, part, imp, p->H, p->L_q, p->L_k, L.plan.nsplit, c, s));
+    FC_TRY(launch_imp_lse_merge(part, lse, p->H, p->L_q, L.plan.nsplit, s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, lse, imp, p->H, p->L_q, p->L_k, c, s));
     return FC_OK;
 }
 
@@ -111,11 +114,7 @@ fc_status chunk_table(const fc_l1_params* p, const int64_t* off, ChunkTable* tab
     return FC_OK;
 }
 
-size_t chunk_ws_bytes(const ChunkTable& tab, size_t* partial_off) {
-    const size_t counters = align_up((size_t)tab.n * sizeof(uint32_t));
-    *partial_off = counters;
-    return counters + align_up((size_t)tab.blk_start[tab.n] * sizeof(float2));
-}
+size_t chunk_ws_bytes(const ChunkTable& tab) { return align_up((size_t)tab.blk_start[tab.n] * sizeof(float2)); }
 
 }  // namespace
 
@@ -176,6 +175,31 @@ fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, 
     const KvLayout L = kv_layout(p);
     if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
     return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void* K, float* lse_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!Q || !K || !lse_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    float2* part = at<float2>(workspace, L.part);
+    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s));
+    FC_TRY(launch_imp_lse_merge(part, lse_out, p->H, p->L_q, L.plan.nsplit, s));
+    return FC_OK;
+}
+
+fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const void* K, const float* lse,
+                                  float* imp_out, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!Q || !K || !lse || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    return hip_status(launch_imp_colsum(dt, p->d, Q, K, lse, imp_out, p->H, p->L_q, p->L_k, log2_scale(p),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, void* workspace,
@@ -251,14 +275,7 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
 size_t fc_chunk_rel_l1_workspace_bytes(const fc_l1_params* p, const int64_t* chunk_offsets) {
     ChunkTable tab;
     if (chunk_table(p, chunk_offsets, &tab) != FC_OK) return 0;
-    size_t po;
-    return chunk_ws_bytes(tab, &po);
-}
-
-fc_status fc_chunk_rel_l1_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-    if (workspace == nullptr || workspace_bytes % 4 != 0) return FC_ERR_INVALID_ARG;
-    return hip_status(launch_zero_u32(static_cast<uint32_t*>(workspace), workspace_bytes / 4,
-                                      static_cast<hipStream_t>(stream)));
+    return chunk_ws_bytes(tab);
 }
 
 fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,
@@ -269,12 +286,10 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
     if (st != FC_OK) return st;
     if (!X_t || !X_tm1 || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
     if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
-    size_t po;
-    const size_t need = chunk_ws_bytes(tab, &po);
-    if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, step, f, recompute, l1_rel_out,
-                                      at<float2>(workspace, po), static_cast<uint32_t*>(workspace), p->m, p->eps,
+                                      static_cast<float2*>(workspace), p->m, p->eps,
                                       static_cast<hipStream_t>(stream)));
 }
 

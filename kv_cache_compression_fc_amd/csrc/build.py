@@ -22,6 +22,8 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (no v_accvgpr_read per element)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

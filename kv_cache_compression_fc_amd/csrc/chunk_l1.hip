@@ -4,13 +4,15 @@
 // and item 2: the first m steps of a chunk recompute with f = 0; afterwards
 // recompute and reset f when f + L1_rel > eps, else accumulate f and reuse.
 //
-// One launch per denoising step.  Each chunk is cut into slabs of a fixed
+// Two launches per denoising step.  Each chunk is cut into slabs of a fixed
 // element count; a workgroup streams one slab of X_t and X_{t-1} with 16-byte
-// loads, reduces sum|X_{t-1} - X_t| and sum|X_t| (float32 per lane, fixed-order
-// wave and block reductions) and writes the pair.  The last workgroup of a
-// chunk to finish (integer ticket) adds the chunk's pairs in slab order (fp64),
+// loads, reduces sum|X_{t-1} - X_t| and sum|X_t| (float32 per lane,
+// fixed-order wave and block reductions) and writes the pair.  A second,
+// one-workgroup-per-chunk kernel adds the chunk's pairs in slab order (fp64),
 // forms L1_rel and updates f, the recompute flag and the step counter on the
-// device, then re-arms the ticket.  HBM-bound: every state byte is read once.
+// device.  The kernel boundary orders the two (no cross-XCD fences or
+// atomics), and the result is deterministic.  HBM-bound: every state byte is
+// read once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,18 +57,13 @@ __device__ __forceinline__ float load_scalar(const void* p, long long i) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void chunk_l1_kernel(ChunkTable tab, const void* __restrict__ X_t,
-                                                            const void* __restrict__ X_tm1,
-                                                            int32_t* __restrict__ step, float* __restrict__ f,
-                                                            uint8_t* __restrict__ recompute,
-                                                            float* __restrict__ l1_out,
-                                                            float2* __restrict__ partial,
-                                                            uint32_t* __restrict__ counters, int m, float eps) {
+__global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable tab, const void* __restrict__ X_t,
+                                                                    const void* __restrict__ X_tm1,
+                                                                    const int32_t* __restrict__ step,
+                                                                    float2* __restrict__ partial) {
     constexpr int V = vec_elems<DT>();
     constexpr long long EPB = slab_elems<DT>();
     __shared__ float red_a[kThreads / kWave], red_n[kThreads / kWave];
-    __shared__ double fin_a[kThreads / kWave], fin_n[kThreads / kWave];
-    __shared__ int is_last;
 
     const int bid = blockIdx.x;
     int lo = 0, hi = tab.n - 1;  // largest chunk c with blk_start[c] <= bid
@@ -75,8 +72,7 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_kernel(ChunkTable tab, cons
         if (tab.blk_start[mid] <= bid) lo = mid; else hi = mid - 1;
     }
     const int c = lo;
-    const int n_step = step[c];
-    if (n_step < 0) return;  // inactive chunk: nothing is read or written
+    if (step[c] < 0) return;  // inactive chunk: nothing is read or written
 
     const long long s0 = tab.off[c] + (long long)(bid - tab.blk_start[c]) * EPB;
     const long long e0 = min(s0 + EPB, tab.off[c + 1]);
@@ -114,16 +110,19 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_kernel(ChunkTable tab, cons
         float ta = 0.f, tn = 0.f;
         for (int w = 0; w < kThreads / kWave; ++w) { ta += red_a[w]; tn += red_n[w]; }
         partial[bid] = make_float2(ta, tn);
-        __threadfence();  // publish the pair before taking a ticket
-        const int nb = tab.blk_start[c + 1] - tab.blk_start[c];
-        const uint32_t ticket = atomicAdd(&counters[c], 1u);
-        is_last = ticket == (uint32_t)(nb - 1);
     }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();  // see every other slab's pair
+}
 
-    // the chunk's pairs in slab order; fp64 for the final sums
+// One workgroup per chunk: L1_rel from the chunk's slab pairs, then the
+// reuse decision.
+__global__ __launch_bounds__(kThreads) void chunk_decide_kernel(ChunkTable tab, const float2* __restrict__ partial,
+                                                                int32_t* __restrict__ step, float* __restrict__ f,
+                                                                uint8_t* __restrict__ recompute,
+                                                                float* __restrict__ l1_out, int m, float eps) {
+    __shared__ double fin_a[kThreads / kWave], fin_n[kThreads / kWave];
+    const int c = blockIdx.x;
+    const int n_step = step[c];
+    if (n_step < 0) return;
     double A = 0.0, N = 0.0;
     for (int b = tab.blk_start[c] + threadIdx.x; b < tab.blk_start[c + 1]; b += kThreads) {
         const float2 p = partial[b];
@@ -132,36 +131,37 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_kernel(ChunkTable tab, cons
     }
     A = wave_sum(A);
     N = wave_sum(N);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) { fin_a[wave] = A; fin_n[wave] = N; }
     __syncthreads();
     if (threadIdx.x == 0) {
         double TA = 0.0, TN = 0.0;
         for (int w = 0; w < kThreads / kWave; ++w) { TA += fin_a[w]; TN += fin_n[w]; }
         const float l1 = TN > 0.0 ? (float)(TA / TN) : INFINITY;
-        float fc_new;
+        float f_new;
         uint8_t rec;
         if (n_step < m) {
-            rec = 1; fc_new = 0.f;
+            rec = 1; f_new = 0.f;                   // forced recompute, f = 0
         } else {
             const float a = f[c] + l1;
-            if (a > eps) { rec = 1; fc_new = 0.f; }
-            else { rec = 0; fc_new = a; }
+            if (a > eps) { rec = 1; f_new = 0.f; }  // recompute and reset
+            else { rec = 0; f_new = a; }            // reuse and accumulate
         }
-        f[c] = fc_new;
+        f[c] = f_new;
         recompute[c] = rec;
         step[c] = n_step + 1;
         if (l1_out) l1_out[c] = l1;
-        counters[c] = 0u;  // re-arm for the next call
     }
 }
 
 template <int DT>
 hipError_t l1_launch(const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step, float* f,
-                     uint8_t* recompute, float* l1_out, float2* partial, uint32_t* counters, int m, float eps,
-                     hipStream_t s) {
+                     uint8_t* recompute, float* l1_out, float2* partial, int m, float eps, hipStream_t s) {
     const int blocks = tab.blk_start[tab.n];
-    hipLaunchKernelGGL(chunk_l1_kernel<DT>, dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1, step, f,
-                       recompute, l1_out, partial, counters, m, eps);
+    hipLaunchKernelGGL(chunk_l1_partial_kernel<DT>, dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1, step,
+                       partial);
+    hipLaunchKernelGGL(chunk_decide_kernel, dim3(tab.n), dim3(kThreads), 0, s, tab, partial, step, f, recompute,
+                       l1_out, m, eps);
     return hipGetLastError();
 }
 
@@ -174,11 +174,10 @@ int chunk_blocks_for(long long elems, int dt) {
 }
 
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step,
-                           float* f, uint8_t* recompute, float* l1_out, float2* partial, uint32_t* counters,
-                           int m, float eps, hipStream_t s) {
-    if (dt == kBF16)
-        return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, counters, m, eps, s);
-    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, counters, m, eps, s);
+                           float* f, uint8_t* recompute, float* l1_out, float2* partial, int m, float eps,
+                           hipStream_t s) {
+    if (dt == kBF16) return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s);
+    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s);
 }
 
 }  // namespace fc

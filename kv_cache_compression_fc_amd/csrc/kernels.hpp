@@ -18,8 +18,11 @@ struct ImpPlan {
 ImpPlan imp_plan(int H, int Lq, int Lk, int dt);
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
                           int Lk, const ImpPlan& plan, float c, hipStream_t s);
-hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float2* part,
-                             float* imp, int H, int Lq, int Lk, int nsplit, float c, hipStream_t s);
+// Pass 2 from the natural-log lse [H][Lq].
+hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* lse, float* imp, int H,
+                             int Lq, int Lk, float c, hipStream_t s);
+// Natural-log lse [H][Lq] from the pass-1 partials.
+hipError_t launch_imp_lse_merge(const float2* part, float* lse, int H, int Lq, int nsplit, hipStream_t s);
 
 // ---- redundancy -------------------------------------------------------------
 // Blocks per head of the two redundancy passes.
@@ -68,6 +71,6 @@ struct ChunkTable {
 int chunk_blocks_for(long long elems, int dt);
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1,
                            int32_t* step, float* f, uint8_t* recompute, float* l1_out, float2* partial,
-                           uint32_t* counters, int m, float eps, hipStream_t s);
+                           int m, float eps, hipStream_t s);
 
 }  // namespace fc

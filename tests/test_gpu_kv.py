@@ -186,3 +186,17 @@ def test_deterministic(fc):
     b = gpu_compress(fc, Q, K, V, 1500, 0.5, 7)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk", [("bf16", 128, 3, 200, 3000), ("f32", 64, 2, 65, 513)])
+def test_importance_two_stages(fc, dtype, d, H, Lq, Lk):
+    # pass 1 (lse) against the oracle's log-sum-exp, then pass 2 fed with it
+    Q, K, _ = synth.random_kv(H, Lq, Lk, d, dtype, seed=12)
+    say(f"case: fc_kv_importance_lse + fc_kv_importance_colsum {dtype} d={d} H={H} Lq={Lq} Lk={Lk}")
+    lse = fc.fc_kv_importance_lse(Q.to(DEV), K.to(DEV))
+    imp = fc.fc_kv_importance_colsum(Q.to(DEV), K.to(DEV), lse)
+    torch.cuda.synchronize()
+    want_lse = oracle.lse(Q, K, 1 / math.sqrt(d))
+    # an absolute lse error e is a relative error e on every exp(s - lse)
+    assert float(np.max(np.abs(lse.cpu().double().numpy() - want_lse))) <= 1e-4
+    assert parity.max_rel_err(imp.cpu().numpy(), oracle.importance(Q, K, 1 / math.sqrt(d))) <= parity.REL
