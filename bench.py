@@ -184,7 +184,7 @@ def main() -> int:
     r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
     fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws)
     t_lse = time_events(lambda: fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws), reps)
-    t_colsum = time_events(lambda: fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp), reps)
+    t_colsum = time_events(lambda: fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp, workspace=ws), reps)
     t_red, how_red = time_graph(lambda: fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws), reps)
     t_sel, how_sel = time_graph(lambda: fc.fc_kv_select(imp, r, B, cfg.lam[0], cfg.w, Kd, Vd, want_scores=False,
                                                         workspace=ws), reps)

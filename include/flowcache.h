@@ -26,7 +26,8 @@
  *   - Outputs must not alias inputs.  Tensors are dense and row-contiguous.
  *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
  *     in [0,1], even pool window, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
- *     128, unknown dtype, too many chunks), FC_ERR_WORKSPACE (workspace null or
+ *     128, unknown dtype, more than 65535 heads, one head's Q or K rows at
+ *     2 GiB or more, too many chunks), FC_ERR_WORKSPACE (workspace null or
  *     smaller than the query), FC_ERR_HIP (a launch failed).  No exception
  *     crosses the ABI.  NaN/Inf inputs are not supported.
  *   - The library keeps no state between calls; calls on different streams
@@ -82,8 +83,8 @@ typedef struct {
 } fc_kv_params;
 
 /* Workspace bytes that fc_kv_compress, fc_kv_importance, fc_kv_importance_lse,
- * fc_kv_redundancy and fc_kv_select need for these parameters (0 if the
- * parameters are invalid). */
+ * fc_kv_importance_colsum, fc_kv_redundancy and fc_kv_select need for these
+ * parameters (0 if the parameters are invalid). */
 size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
 
 /*
@@ -130,11 +131,12 @@ fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void*
 /*
  * fc_kv_importance_colsum -- the second pass alone, given the normalisers:
  *   imp_out[h][j] = (1/L_q) sum_i exp(scale q_i.k_j - lse[h][i]).
- * lse [H][L_q] f32 device (natural log, as written by fc_kv_importance_lse);
- * one kernel launch, no workspace.
+ * lse [H][L_q] f32 device (natural log, as written by fc_kv_importance_lse).
+ * The workspace (same size query) receives the normalisers in the kernel's
+ * own form before the pass.
  */
 fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const void* K, const float* lse,
-                                  float* imp_out, void* stream);
+                                  float* imp_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fc_kv_redundancy -- mean cosine similarity before its softmax:

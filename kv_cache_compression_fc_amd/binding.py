@@ -62,7 +62,7 @@ _lib.fc_kv_importance.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _
 _lib.fc_kv_importance_lse.restype = ctypes.c_int
 _lib.fc_kv_importance_lse.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_importance_colsum.restype = ctypes.c_int
-_lib.fc_kv_importance_colsum.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _vp]
+_lib.fc_kv_importance_colsum.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_redundancy.restype = ctypes.c_int
 _lib.fc_kv_redundancy.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_select.restype = ctypes.c_int
@@ -181,13 +181,15 @@ def fc_kv_importance_lse(Q, K, softmax_scale: float = 0.0, lse_out=None, workspa
     return lse_out
 
 
-def fc_kv_importance_colsum(Q, K, lse, softmax_scale: float = 0.0, imp_out=None, stream=None):
+def fc_kv_importance_colsum(Q, K, lse, softmax_scale: float = 0.0, imp_out=None, workspace=None, stream=None):
     p = kv_params(Q, K, 1, 0.5, 1, softmax_scale)
     H, Lk, _ = K.shape
     if imp_out is None:
         imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance_colsum", _lib.fc_kv_importance_colsum(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse),
-                                                                   _ptr(imp_out), _stream(stream)))
+                                                                   _ptr(imp_out), _ptr(ws), ws.numel(),
+                                                                   _stream(stream)))
     return imp_out
 
 

@@ -20,7 +20,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct KvLayout {
     ImpPlan plan;
     int nbu, nbr, nbs;
-    size_t part, lse, imp, r, u_part, red_part, keys, hist, counts, state, total;
+    size_t part, nlse2, imp, r, u_part, red_part, keys, hist, counts, state, total;
 };
 
 fc_status check_kv(const fc_kv_params* p) {
@@ -32,6 +32,10 @@ fc_status check_kv(const fc_kv_params* p) {
     if (p->dtype != FC_F32 && p->dtype != FC_BF16) return FC_ERR_UNSUPPORTED;
     if (p->d != 64 && p->d != 128) return FC_ERR_UNSUPPORTED;
     if (p->H > 65535) return FC_ERR_UNSUPPORTED;
+    // one head's Q or K rows are addressed with 32-bit byte offsets
+    const long long esize = p->dtype == FC_BF16 ? 2 : 4;
+    if ((long long)p->L_q * p->d * esize >= (1LL << 31) || (long long)p->L_k * p->d * esize >= (1LL << 31))
+        return FC_ERR_UNSUPPORTED;
     return FC_OK;
 }
 
@@ -45,7 +49,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
-    L.lse = o;      o = align_up(o + H * (size_t)p->L_q * sizeof(float));
+    L.nlse2 = o;    o = align_up(o + H * (size_t)imp_lq_pad(p->L_q) * sizeof(float));
     L.imp = o;      o = align_up(o + H * Lk * sizeof(float));
     L.r = o;        o = align_up(o + H * Lk * sizeof(float));
     L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
@@ -84,10 +88,10 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const float c = log2_scale(p);
     float2* part = at<float2>(ws, L.part);
-    float* lse = at<float>(ws, L.lse);
+    float* nlse2 = at<float>(ws, L.nlse2);
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
-    FC_TRY(launch_imp_lse_merge(part, lse, p->H, p->L_q, L.plan.nsplit, s));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, lse, imp, p->H, p->L_q, p->L_k, c, s));
+    FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp, p->H, p->L_q, p->L_k, c, s));
     return FC_OK;
 }
 
@@ -163,7 +167,8 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
     // pool + score + top-B + gather
     FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
                                     red_out, sb, p->H, p->L_k, s));
-    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, dt, p->d, K, V, K_out, V_out, idx_out, s));
+    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, idx_out, s));
+    FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
 }
 
@@ -188,18 +193,23 @@ fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void*
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float2* part = at<float2>(workspace, L.part);
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s));
-    FC_TRY(launch_imp_lse_merge(part, lse_out, p->H, p->L_q, L.plan.nsplit, s));
+    FC_TRY(launch_imp_lse_merge(part, lse_out, nullptr, p->H, p->L_q, L.plan.nsplit, s));
     return FC_OK;
 }
 
 fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const void* K, const float* lse,
-                                  float* imp_out, void* stream) {
+                                  float* imp_out, void* workspace, size_t workspace_bytes, void* stream) {
     fc_status st = check_kv(p);
     if (st != FC_OK) return st;
     if (!Q || !K || !lse || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
-    return hip_status(launch_imp_colsum(dt, p->d, Q, K, lse, imp_out, p->H, p->L_q, p->L_k, log2_scale(p),
-                                        static_cast<hipStream_t>(stream)));
+    float* nlse2 = at<float>(workspace, L.nlse2);
+    FC_TRY(launch_imp_nlse2(lse, nlse2, p->H, p->L_q, s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp_out, p->H, p->L_q, p->L_k, log2_scale(p), s));
+    return FC_OK;
 }
 
 fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, void* workspace,
@@ -237,7 +247,8 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
     FC_TRY(launch_red_stats(r, red_part, p->H, p->L_k, sb.hist, kHistWordsPerHead, s));
     FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
                                     red_out, sb, p->H, p->L_k, s));
-    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, dt, p->d, gather ? K : nullptr, V, K_out, V_out, idx_out, s));
+    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, idx_out, s));
+    if (gather) FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
 }
 
@@ -268,7 +279,7 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
     const int Bp = B < L ? B : L;
     FC_TRY(launch_zero_u32(sb.hist, h * kHistWordsPerHead, s));
     FC_TRY(launch_sel_keys_from_scores(scores, sb, H, L, s));
-    FC_TRY(launch_sel_finish(sb, H, L, Bp, kF32, 64, nullptr, nullptr, nullptr, nullptr, idx_out, s));
+    FC_TRY(launch_sel_finish(sb, H, L, Bp, idx_out, s));
     return FC_OK;
 }
 

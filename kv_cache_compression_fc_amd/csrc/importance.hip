@@ -4,16 +4,33 @@
 // queries.  Per head h:
 //     Imp_j = (1/L_q) sum_i exp(s_ij - lse_i),   s_ij = scale * q_i . k_j,
 //     lse_i = log sum_j exp(s_ij).
-// Two passes over Q K^T, both on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
-// accumulate), neither materialising the L_q x L_k matrix:
-//   pass 1 (imp_lse_kernel)    a workgroup owns 128 queries, streams K tiles
-//                              through LDS and keeps a per-lane online
-//                              (max, sum of 2^x) in base 2;
-//   pass 2 (imp_colsum_kernel) a workgroup owns 128 keys, streams Q tiles and
-//                              their -lse through LDS, recomputes the logits
-//                              and accumulates column sums of 2^(x - lse2)
-//                              in registers.  No atomics: deterministic.
-// The scale is folded with log2(e) into one FMA before v_exp_f32.
+// Two passes over Q K^T on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulate); neither materialises the L_q x L_k matrix:
+//   pass 1 (imp_lse_kernel)    a workgroup owns 256 queries and one range of
+//                              keys, streams K tiles through LDS and sums
+//                              2^(x - m) per query, x = scale*log2(e) q.k;
+//   pass 2 (imp_colsum_kernel) a workgroup owns 256 keys, streams Q tiles
+//                              and their -lse2 through LDS, recomputes the
+//                              logits and accumulates column sums of
+//                              2^(x - lse2) in registers.
+// Layout and scheduling for gfx950:
+//   * 8 waves per workgroup, one register-resident 32-row operand block per
+//     wave and at most 128 VGPRs, so four waves share each SIMD and the
+//     vector work of one wave (one FMA, one v_exp_f32 and one add per logit)
+//     fills the MFMA shadow of the others;
+//   * the streamed tiles go global -> LDS directly (buffer_load ... lds, no
+//     registers), three buffers deep, so each tile is requested two tiles
+//     before it is used; rows past the end read as zero;
+//   * LDS tiles are unpadded with an XOR swizzle of the 16-byte chunks, so the
+//     16-byte fragment reads of 16 consecutive rows hit distinct banks;
+//   * inside a tile the MFMAs of block 1 are interleaved with the
+//     exponentials of block 0.
+// Pass 1 does not track a running maximum: the shift m is the maximum over the
+// range's first 32 keys, and a workgroup whose sums leave the safe range (a
+// logit more than ~100 binary orders above m) redoes its range with an exact
+// running maximum.  No atomics: the result is deterministic.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,47 +38,112 @@ namespace fc {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kNB = 2;                           // register-resident 32-row blocks per wave
-constexpr int kRowsPerWave = 32 * kNB;
-constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // 256 queries (pass 1) or keys (pass 2)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+// __launch_bounds__ minimum waves per SIMD: four caps bf16 kernels at 128
+// VGPRs; fp32 operand blocks are twice as large and run two.
+template <int DT> constexpr int min_waves_per_simd() { return DT == kBF16 ? 4 : 2; }
+constexpr int kRowsPerBlock = kWaves * 32;    // 256 queries (pass 1) or keys (pass 2)
+constexpr int kNBuf = 3;                      // LDS tile buffers
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
+// A byte offset past every resource built here (a head's rows are < 2^31
+// bytes, checked on the host, plus < 2^16 bytes of in-tile offsets).
+constexpr uint32_t kNoRecord = 0x80000000u;
 
-// Global -> registers -> LDS staging of a ROWS x D tile of row-major data,
-// 16 bytes per thread per step.  LDS rows are padded by 16 bytes so that the
-// 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+// Byte-addressed view of one head's rows for buffer loads: reads at or past
+// num_bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, (int)kRsrcWord3);
+}
+
+template <int DT> constexpr int tile_rows() { return DT == kBF16 ? 64 : 32; }
+
+// A ROWS x D tile in LDS: rows of D*E bytes, 16-byte chunks XOR-swizzled so
+// that the same logical chunk of 16 consecutive rows lands in 16 distinct
+// bank groups.  Loaded straight from global memory by buffer_load ... lds: a
+// wave instruction writes 1 KiB of consecutive LDS, lane i to chunk i, so
+// each lane fetches the global chunk that the swizzle puts there.
 template <int DT, int D, int ROWS>
-struct TileStager {
-    static constexpr int kE = Elem<DT>::kBytes;
-    static constexpr int kRowBytes = D * kE;
-    static constexpr int kChunksPerRow = kRowBytes / 16;
-    static constexpr int kPerThread = ROWS * kChunksPerRow / kThreads;
-    static constexpr int kRowStride = kRowBytes + 16;
-    static constexpr int kBytes = ROWS * kRowStride;
-    static_assert(ROWS * kChunksPerRow % kThreads == 0, "tile must split evenly over the block");
-    uint4 regs[kPerThread];
+struct SwizzledTile {
+    static constexpr int kRowBytes = D * Elem<DT>::kBytes;
+    static constexpr int kCpr = kRowBytes / 16;                 // chunks per row
+    static constexpr int kBytes = ROWS * kRowBytes;
+    static constexpr int kWaveLoads = ROWS * kCpr / kWave;      // 1 KiB wave loads per tile
+    static constexpr int kLoadsPerWave = kWaveLoads / kWaves;
+    static constexpr int kRowGroup = kCpr >= 16 ? 1 : 16 / kCpr;
+    static constexpr int kSwzMod = kCpr >= 16 ? 16 : kCpr;
+    static_assert(kLoadsPerWave >= 1 && kWaveLoads % kWaves == 0, "tile must split evenly over the waves");
 
-    // rows_valid may be <= 0 or > ROWS; rows beyond it are zero-filled.
-    __device__ __forceinline__ void load(const char* gtile, int rows_valid) {
+    __device__ static __forceinline__ int swz(int r) { return (r / kRowGroup) % kSwzMod; }
+    __device__ static __forceinline__ int offset(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
+
+    // This wave's share of the tile whose first row is at byte `off` of `rs`.
+    __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int wave,
+                                                 int lane) {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int c = threadIdx.x + kThreads * i;
-            const int row = c / kChunksPerRow, col = c % kChunksPerRow;
-            regs[i] = row < rows_valid
-                          ? *reinterpret_cast<const uint4*>(gtile + (size_t)row * kRowBytes + col * 16)
-                          : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int c = threadIdx.x + kThreads * i;
-            const int row = c / kChunksPerRow, col = c % kChunksPerRow;
-            *reinterpret_cast<uint4*>(lds + row * kRowStride + col * 16) = regs[i];
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+            const int wl = wave * kLoadsPerWave + j;
+            const int p = wl * kWave + lane;
+            const int r = p / kCpr, c = (p % kCpr) ^ swz(p / kCpr);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, buf + wl * 1024, 16, off + r * kRowBytes + c * 16, 0, 0, 0);
         }
     }
 };
 
-template <int DT> constexpr int tile_rows() { return DT == kBF16 ? 64 : 32; }
+// Byte offsets, inside a swizzled tile, of the fragments this lane reads for
+// a 32-row block: row lane%32, elements 16*kk + 8*(lane/32) .. +8 (fp32: two
+// 16-byte chunks).  The swizzle repeats every 16 rows, so a block starting at
+// row r0 (a multiple of 16) reads at r0 * kRowBytes + these offsets: computed
+// once per lane, independent of the buffer, and each LDS read is then one
+// register plus an immediate.
+template <int DT, int D, int ROWS>
+struct FragOffsets {
+    using T = SwizzledTile<DT, D, ROWS>;
+    static constexpr int NKK = D / 16;
+    static constexpr int kParts = DT == kBF16 ? 1 : 2;
+    static_assert(T::kRowGroup * T::kSwzMod == 16, "swizzle period must be 16 rows");
+    int o[NKK * kParts];
+    __device__ __forceinline__ explicit FragOffsets(int lane) {
+        const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int p = 0; p < kParts; ++p) o[kk * kParts + p] = T::offset(r, kParts * (2 * kk + half) + p);
+    }
+};
+
+template <int DT, int D, int ROWS>
+__device__ __forceinline__ void load_frag(Frag8<DT>& f, const char* blk, const FragOffsets<DT, D, ROWS>& fo, int kk) {
+    if constexpr (DT == kBF16) {
+        f.u = *reinterpret_cast<const uint4*>(blk + fo.o[kk]);
+    } else {
+        f.lo = *reinterpret_cast<const float4*>(blk + fo.o[2 * kk]);
+        f.hi = *reinterpret_cast<const float4*>(blk + fo.o[2 * kk + 1]);
+    }
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    // gfx9 encoding: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] in [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the tile pipeline.  __syncthreads() would also wait
+// for every LDS-DMA load in flight (they count as LDS stores), which drains
+// the prefetch of the next-but-one tile; the waits before this barrier are
+// explicit (wait_vmcnt for the tile about to be read; the compiler's lgkmcnt
+// waits retire this wave's LDS reads before their results feed the MFMAs).
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int B> using Buf = std::integral_constant<int, B>;
 
 // The hardware hands linear block b to XCD b % 8.  Give every XCD a
 // contiguous range of logical work items, so that the blocks running together
@@ -70,17 +152,66 @@ __device__ __forceinline__ int xcd_item(int per_xcd) {
     return (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
 }
 
+#define FC_SB() __builtin_amdgcn_sched_barrier(0)
+
+// acc = (32 streamed rows starting at row r0 of the tile) x (register operand):
+// a 32x32 fp32 tile.  Fragment reads run half a block ahead of the MFMAs
+// that consume them; with `slice` each MFMA
+// is followed, in a fixed order, by vector work on another block (16/NKK of
+// its rows), so that work runs in the MFMA shadow.
+template <int DT, int D, int ROWS, typename Slice>
+__device__ __forceinline__ void mfma_block(f32x16_t& acc, const char* buf, int r0, const FragOffsets<DT, D, ROWS>& fo,
+                                           const Frag8<DT> (&b)[D / 16], Slice&& slice) {
+    constexpr int NKK = D / 16;
+    constexpr int P = NKK / 2;  // fragment reads kept ahead of the MFMA that uses them
+    const char* blk = buf + r0 * SwizzledTile<DT, D, ROWS>::kRowBytes;
+    Frag8<DT> a[NKK];
+#pragma unroll
+    for (int kk = 0; kk < P; ++kk) load_frag<DT, D, ROWS>(a[kk], blk, fo, kk);
+    acc = f32x16_t{};
+    FC_SB();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + P < NKK) load_frag<DT, D, ROWS>(a[kk + P], blk, fo, kk + P);
+        mfma16(acc, a[kk], b[kk]);
+        FC_SB();
+        slice(kk * (16 / NKK), 16 / NKK);
+        FC_SB();
+    }
+}
+struct NoSlice {
+    __device__ void operator()(int, int) const {}
+};
+
+// Masks logits of streamed rows at or past `valid` (relative to the block).
+__device__ __forceinline__ void mask_rows(f32x16_t& acc, int valid, int half) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * half + (r & 3) >= valid) acc[r] = -INFINITY;
+}
+
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void imp_lse_kernel(const void* __restrict__ Q,
-                                                           const void* __restrict__ K,
-                                                           float2* __restrict__ part, int Lq, int Lk,
-                                                           int keys_per_split, int nsplit, int nqb,
-                                                           int n_items, float c) {
+__global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_kernel(const void* __restrict__ Q,
+                                                                            const void* __restrict__ K,
+                                                                            float2* __restrict__ part, int Lq,
+                                                                            int Lk, int keys_per_split, int nsplit,
+                                                                            int nqb, int n_items, float c) {
     constexpr int kE = Elem<DT>::kBytes;
     constexpr int KT = tile_rows<DT>();
     constexpr int NKK = D / 16;
-    using Stager = TileStager<DT, D, KT>;
-    __shared__ __align__(16) char lds[2][Stager::kBytes];
+    using Tile = SwizzledTile<DT, D, KT>;
+    constexpr int L = Tile::kLoadsPerWave;
+    // One LDS array per buffer, each named at compile time (the tile loop is
+    // unrolled by kNBuf): the compiler can then tell a buffer being read from
+    // the buffer an LDS-DMA load is filling, and does not wait for that load.
+    __shared__ __align__(1024) char lds0[Tile::kBytes];
+    __shared__ __align__(1024) char lds1[Tile::kBytes];
+    __shared__ __align__(1024) char lds2[Tile::kBytes];
+    auto lds = [&](auto b) -> char* {
+        if constexpr (decltype(b)::value == 0) return lds0;
+        else if constexpr (decltype(b)::value == 1) return lds1;
+        else return lds2;
+    };
 
     const int item = xcd_item((n_items + 7) / 8);
     if (item >= n_items) return;
@@ -89,92 +220,133 @@ __global__ __launch_bounds__(kThreads) void imp_lse_kernel(const void* __restric
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5;
-    const int q0 = qblk * kRowsPerBlock + wave * kRowsPerWave + (lane & 31);
+    const FragOffsets<DT, D, KT> fo(lane);
+    const int q = qblk * kRowsPerBlock + wave * 32 + (lane & 31);
     const char* Qh = static_cast<const char*>(Q) + (size_t)h * Lq * D * kE;
-    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
-
-    // Q^T fragments (B operand) of this wave's kNB query blocks.
-    Frag8<DT> qf[kNB][NKK];
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        const int q = q0 + 32 * nb;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            if (q < Lq) qf[nb][kk].load(Qh + ((size_t)q * D + 16 * kk + 8 * half) * kE);
-            else qf[nb][kk].zero();
-        }
-    }
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(static_cast<const char*>(K) + (size_t)h * Lk * D * kE,
+                                                 (uint32_t)Lk * D * kE);
 
     const int k_begin = split * keys_per_split;
-    const int k_end = min(Lk, k_begin + keys_per_split);
-    const int ntiles = (k_end - k_begin + KT - 1) / KT;
+    const int nkeys = min(Lk, k_begin + keys_per_split) - k_begin;  // >= 1
+    const int ntiles = (nkeys + KT - 1) / KT;
+    const uint32_t off0 = (uint32_t)k_begin * D * kE;
+    const uint32_t tile_bytes = KT * D * kE;
 
-    // Per query block: this lane's keys so far, sum 2^(x - m) with x = c q.k.
-    float m[kNB], s[kNB];
+    // Tiles 0 and 1 in flight while the Q fragments load.
+    Tile::issue(krs, off0, lds(Buf<0>{}), wave, lane);
+    Tile::issue(krs, ntiles > 1 ? off0 + tile_bytes : kNoRecord, lds(Buf<1>{}), wave, lane);
+
+    // Q^T fragments (B operand): query q, depth 16*kk + 8*half .. +8.
+    Frag8<DT> qf[NKK];
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) { m[nb] = -1e30f; s[nb] = 0.f; }
-    Stager st;
-    st.load(Kh + (size_t)k_begin * D * kE, k_end - k_begin);
-    st.store(lds[0]);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int kt0 = k_begin + t * KT;
-        if (t + 1 < ntiles) st.load(Kh + (size_t)(kt0 + KT) * D * kE, k_end - (kt0 + KT));
-        const char* L = lds[t & 1];
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (q < Lq) qf[kk].load(Qh + ((size_t)q * D + 16 * kk + 8 * half) * kE);
+        else qf[kk].zero();
+    }
+    wait_vmcnt<L>();  // tile 0 landed (tile 1 may be in flight)
+    tile_barrier();
+
+    // Shift: the maximum logit over the first 32 keys of the range (exact,
+    // masked), per query.
+    float nm;
+    {
+        f32x16_t acc;
+        mfma_block<DT, D, KT>(acc, lds(Buf<0>{}), 0, fo, qf, NoSlice{});
+        mask_rows(acc, nkeys, half);
+        float t = acc[0];
 #pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) {
-            if (kt0 + kb * 32 >= k_end) break;  // uniform over the block
-            f32x16_t acc[kNB];
+        for (int r = 1; r < 16; ++r) t = fmaxf(t, acc[r]);
+        t = fmaxf(t, __shfl_xor(t, 32, kWave));
+        nm = -t * c;
+    }
+
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    auto acc_rows = [&](const f32x16_t& acc, int r0, int nr) {
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x16_t{};
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                Frag8<DT> a;
-                a.load(L + (kb * 32 + (lane & 31)) * Stager::kRowStride + (16 * kk + 8 * half) * kE);
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) mfma16(acc[nb], a, qf[nb][kk]);
-            }
-            // acc[nb][r] = k_j . q with j = kt0 + 32*kb + 8*(r/4) + 4*half + r%4.
-            if (kt0 + kb * 32 + 32 > k_end) {
-                const int j0 = kt0 + kb * 32 + 4 * half;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (j0 + 8 * (r >> 2) + (r & 3) >= k_end) {
-#pragma unroll
-                        for (int nb = 0; nb < kNB; ++nb) acc[nb][r] = -INFINITY;
-                    }
-            }
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                float tmax = fmaxf(fmaxf(acc[nb][0], acc[nb][1]), acc[nb][2]);
-#pragma unroll
-                for (int r = 3; r < 15; r += 2) tmax = fmaxf(fmaxf(tmax, acc[nb][r]), acc[nb][r + 1]);
-                tmax = fmaxf(tmax, acc[nb][15]);
-                const float mn = fmaxf(m[nb], tmax * c);
-                float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; r += 4) {
-                    p0 += exp2_hw(fmaf(acc[nb][r + 0], c, -mn));
-                    p1 += exp2_hw(fmaf(acc[nb][r + 1], c, -mn));
-                    p2 += exp2_hw(fmaf(acc[nb][r + 2], c, -mn));
-                    p3 += exp2_hw(fmaf(acc[nb][r + 3], c, -mn));
-                }
-                s[nb] = fmaf(s[nb], exp2_hw(m[nb] - mn), (p0 + p1) + (p2 + p3));
-                m[nb] = mn;
-            }
+        for (int r = r0; r < r0 + nr; ++r) {
+            const float p = exp2_hw(fmaf(acc[r], c, nm));
+            if ((r & 3) == 0) s0 += p; else if ((r & 3) == 1) s1 += p; else if ((r & 3) == 2) s2 += p; else s3 += p;
         }
-        if (t + 1 < ntiles) st.store(lds[(t + 1) & 1]);
-        __syncthreads();
+    };
+    // Tile t is read from buffer t % 3; tile t+2 goes into the buffer tile t-1
+    // used, which every wave has left (barrier at the end of step t-1).
+    auto step = [&](auto b, int t) {
+        constexpr int B = decltype(b)::value;
+        // Past the last tile the offset lies outside the resource: the load
+        // moves no data (zeros land in a buffer nobody reads), and every step
+        // issues the same loads, so the waits below stay uniform.
+        Tile::issue(krs, t + 2 < ntiles ? off0 + (uint32_t)(t + 2) * tile_bytes : kNoRecord,
+                    lds(Buf<(B + 2) % kNBuf>{}), wave, lane);
+        const char* buf = lds(b);
+        const int valid = nkeys - t * KT;  // rows of this tile inside the range
+        if constexpr (KT == 64) {
+            f32x16_t a0, a1;
+            mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, NoSlice{});
+            if (valid < 32) mask_rows(a0, valid, half);
+            if (valid > 32) {
+                mfma_block<DT, D, KT>(a1, buf, 32, fo, qf, [&](int r0, int nr) { acc_rows(a0, r0, nr); });
+                if (valid < 64) mask_rows(a1, valid - 32, half);
+                acc_rows(a1, 0, 16);
+            } else {
+                acc_rows(a0, 0, 16);
+            }
+        } else {
+            f32x16_t a0;
+            mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, NoSlice{});
+            if (valid < 32) mask_rows(a0, valid, half);
+            acc_rows(a0, 0, 16);
+        }
+        wait_vmcnt<L>();  // tile t+1 landed, tile t+2 may be in flight
+        tile_barrier();
+    };
+    // Whole rounds of three tiles, then the tail: the loop's back edge then
+    // only follows a buffer-2 step, so the compiler sees on every path which
+    // loads the explicit waits have retired and adds no waits of its own.
+    int t = 0;
+    for (; t + 2 < ntiles; t += kNBuf) {
+        step(Buf<0>{}, t);
+        step(Buf<1>{}, t + 1);
+        step(Buf<2>{}, t + 2);
     }
+    if (t < ntiles) {
+        step(Buf<0>{}, t);
+        if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
+    }
+    wait_vmcnt<0>();
+
+    float m = -nm, tot = (s0 + s1) + (s2 + s3);
+    if (__syncthreads_or(!(tot < 0x1p100f))) {  // overflow (or NaN) under the fixed shift
+        // Exact path for this range: running maximum per block of 32 keys.
+        m = -1e30f;
+        tot = 0.f;
+        for (int t = 0; t < ntiles; ++t) {
+            Tile::issue(krs, off0 + (uint32_t)t * tile_bytes, lds(Buf<0>{}), wave, lane);
+            wait_vmcnt<0>();
+            __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        // Lanes l and l^32 hold disjoint key subsets of the same query.
-        float mm = m[nb], ss = s[nb];
-        const float m2 = __shfl_xor(mm, 32, kWave), s2 = __shfl_xor(ss, 32, kWave);
-        lse2_merge(mm, ss, m2, s2);
-        const int q = q0 + 32 * nb;
-        if (lane < 32 && q < Lq) part[((size_t)h * nsplit + split) * Lq + q] = make_float2(mm, ss);
+            for (int kb = 0; kb < KT / 32; ++kb) {
+                const int valid = nkeys - t * KT - kb * 32;
+                if (valid <= 0) break;
+                f32x16_t acc;
+                mfma_block<DT, D, KT>(acc, lds(Buf<0>{}), kb * 32, fo, qf, NoSlice{});
+                mask_rows(acc, valid, half);
+                float tmax = acc[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+                const float mn = fmaxf(m, tmax * c);
+                float p = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p += exp2_hw(fmaf(acc[r], c, -mn));
+                tot = fmaf(tot, exp2_hw(m - mn), p);
+                m = mn;
+            }
+            __syncthreads();
+        }
     }
+    // Lanes l and l^32 hold disjoint key subsets of the same query.
+    const float m2 = __shfl_xor(m, 32, kWave), t2 = __shfl_xor(tot, 32, kWave);
+    lse2_merge(m, tot, m2, t2);
+    if (lane < 32 && q < Lq) part[((size_t)h * nsplit + split) * Lq + q] = make_float2(m, tot);
 }
 
 // lse of query q in base 2 (log2 sum_j 2^(c s_ij)), merged over the key splits.
@@ -187,26 +359,58 @@ __device__ __forceinline__ float merged_lse2(const float2* __restrict__ ph, int 
     return m + log2_hw(s);
 }
 
-// Natural-log lse of each query from the pass-1 partials.
-__global__ __launch_bounds__(kThreads) void imp_lse_merge_kernel(const float2* __restrict__ part,
-                                                                 float* __restrict__ lse, int Lq, int nsplit) {
+constexpr int kSmallThreads = 256;
+
+// Per query: the natural-log lse (optional) and -lse2 padded with -inf to
+// lq_pad (optional), from the pass-1 partials.
+__global__ __launch_bounds__(kSmallThreads) void imp_lse_merge_kernel(const float2* __restrict__ part,
+                                                                      float* __restrict__ lse,
+                                                                      float* __restrict__ nlse2, int Lq, int lq_pad,
+                                                                      int nsplit) {
     const int h = blockIdx.y;
-    const int q = blockIdx.x * kThreads + threadIdx.x;
-    if (q < Lq) lse[(size_t)h * Lq + q] = merged_lse2(part + (size_t)h * nsplit * Lq, Lq, nsplit, q) / kLog2e;
+    const int q = blockIdx.x * kSmallThreads + threadIdx.x;
+    if (q >= lq_pad) return;
+    const float l2 = q < Lq ? merged_lse2(part + (size_t)h * nsplit * Lq, Lq, nsplit, q) : INFINITY;
+    if (lse && q < Lq) lse[(size_t)h * Lq + q] = l2 / kLog2e;
+    if (nlse2) nlse2[(size_t)h * lq_pad + q] = -l2;
+}
+
+// -lse2 padded with -inf from a natural-log lse.
+__global__ __launch_bounds__(kSmallThreads) void imp_nlse2_kernel(const float* __restrict__ lse,
+                                                                  float* __restrict__ nlse2, int Lq, int lq_pad) {
+    const int h = blockIdx.y;
+    const int q = blockIdx.x * kSmallThreads + threadIdx.x;
+    if (q < lq_pad) nlse2[(size_t)h * lq_pad + q] = q < Lq ? -lse[(size_t)h * Lq + q] * kLog2e : -INFINITY;
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void imp_colsum_kernel(const void* __restrict__ Q,
-                                                              const void* __restrict__ K,
-                                                              const float* __restrict__ lse,
-                                                              float* __restrict__ imp, int Lq, int Lk, int nkb,
-                                                              int n_items, float c, float inv_lq) {
+__global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum_kernel(const void* __restrict__ Q,
+                                                                               const void* __restrict__ K,
+                                                                               const float* __restrict__ nlse2,
+                                                                               float* __restrict__ imp, int Lq,
+                                                                               int lq_pad, int Lk, int nkb,
+                                                                               int n_items, float c, float inv_lq) {
     constexpr int kE = Elem<DT>::kBytes;
     constexpr int QT = tile_rows<DT>();
     constexpr int NKK = D / 16;
-    using Stager = TileStager<DT, D, QT>;
-    __shared__ __align__(16) char lds[2][Stager::kBytes];
-    __shared__ __align__(16) float nlse[2][QT];  // -lse2 of the tile's queries (-inf past L_q)
+    using Tile = SwizzledTile<DT, D, QT>;
+    constexpr int L = Tile::kLoadsPerWave + 1;  // + the load of the tile's -lse2
+    // Per buffer: a Q tile and the tile's -lse2 (64 floats, QT <= 64), each a
+    // separate LDS array named at compile time (see imp_lse_kernel).
+    __shared__ __align__(1024) char lds0[Tile::kBytes];
+    __shared__ __align__(1024) char lds1[Tile::kBytes];
+    __shared__ __align__(1024) char lds2[Tile::kBytes];
+    __shared__ float nl0[kWave], nl1[kWave], nl2[kWave];
+    auto lds = [&](auto b) -> char* {
+        if constexpr (decltype(b)::value == 0) return lds0;
+        else if constexpr (decltype(b)::value == 1) return lds1;
+        else return lds2;
+    };
+    auto nl_lds = [&](auto b) -> float* {
+        if constexpr (decltype(b)::value == 0) return nl0;
+        else if constexpr (decltype(b)::value == 1) return nl1;
+        else return nl2;
+    };
 
     const int item = xcd_item((n_items + 7) / 8);
     if (item >= n_items) return;
@@ -214,81 +418,84 @@ __global__ __launch_bounds__(kThreads) void imp_colsum_kernel(const void* __rest
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5;
-    const int key0 = kblk * kRowsPerBlock + wave * kRowsPerWave + (lane & 31);
-    const char* Qh = static_cast<const char*>(Q) + (size_t)h * Lq * D * kE;
+    const FragOffsets<DT, D, QT> fo(lane);
+    const int key = kblk * kRowsPerBlock + wave * 32 + (lane & 31);
+    const __amdgpu_buffer_rsrc_t qrs = head_rsrc(static_cast<const char*>(Q) + (size_t)h * Lq * D * kE,
+                                                 (uint32_t)Lq * D * kE);
+    const __amdgpu_buffer_rsrc_t nrs = head_rsrc(nlse2 + (size_t)h * lq_pad, (uint32_t)lq_pad * 4);
     const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
-    const float* lse_h = lse + (size_t)h * Lq;
-
-    // K^T fragments (B operand) of this wave's kNB key blocks.
-    Frag8<DT> kf[kNB][NKK];
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        const int key = key0 + 32 * nb;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            if (key < Lk) kf[nb][kk].load(Kh + ((size_t)key * D + 16 * kk + 8 * half) * kE);
-            else kf[nb][kk].zero();
-        }
-    }
-
     const int ntiles = (Lq + QT - 1) / QT;
-    float cs[kNB][4];
+    const uint32_t tile_bytes = QT * D * kE;
+
+    // Tile t into buffer b = t % 3: Q rows (all waves share the copy) and its
+    // -lse2 (4 bytes per lane; every wave writes the same values, so the
+    // per-wave load counts match and the copy needs no extra synchronisation).
+    // Tiles past the last are issued with an offset outside the resources
+    // (no data moves), as in imp_lse_kernel.
+    auto issue = [&](auto b, int t) {
+        const bool real = t < ntiles;
+        Tile::issue(qrs, real ? (uint32_t)t * tile_bytes : kNoRecord, lds(b), wave, lane);
+        const int qi = t * QT + (lane < QT ? lane : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(nrs, nl_lds(b), 4, real ? (uint32_t)qi * 4 : kNoRecord, 0, 0, 0);
+    };
+    issue(Buf<0>{}, 0);
+    issue(Buf<1>{}, 1);  // (out of range when there is one tile)
+
+    // K^T fragments (B operand): key, depth 16*kk + 8*half .. +8.
+    Frag8<DT> kf[NKK];
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) cs[nb][0] = cs[nb][1] = cs[nb][2] = cs[nb][3] = 0.f;
-    Stager st;
-    st.load(Qh, Lq);
-    st.store(lds[0]);
-    if (threadIdx.x < QT) nlse[0][threadIdx.x] = (int)threadIdx.x < Lq ? -lse_h[threadIdx.x] * kLog2e : -INFINITY;
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int qt0 = t * QT;
-        float lse_next = INFINITY;
-        if (t + 1 < ntiles) {
-            st.load(Qh + (size_t)(qt0 + QT) * D * kE, Lq - (qt0 + QT));
-            const int qn = qt0 + QT + threadIdx.x;
-            if (threadIdx.x < QT && qn < Lq) lse_next = lse_h[qn];
-        }
-        const char* L = lds[t & 1];
-        const float* NL = nlse[t & 1];
-#pragma unroll
-        for (int qb = 0; qb < QT / 32; ++qb) {
-            f32x16_t acc[kNB];
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x16_t{};
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                Frag8<DT> a;
-                a.load(L + (qb * 32 + (lane & 31)) * Stager::kRowStride + (16 * kk + 8 * half) * kE);
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) mfma16(acc[nb], a, kf[nb][kk]);
-            }
-            // acc[nb][r] = q_i . k with i = qt0 + 32*qb + 8*(r/4) + 4*half + r%4.
-            const float* nl = NL + qb * 32 + 4 * half;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 n = *reinterpret_cast<const float4*>(nl + 8 * g);
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    cs[nb][0] += exp2_hw(fmaf(acc[nb][4 * g + 0], c, n.x));
-                    cs[nb][1] += exp2_hw(fmaf(acc[nb][4 * g + 1], c, n.y));
-                    cs[nb][2] += exp2_hw(fmaf(acc[nb][4 * g + 2], c, n.z));
-                    cs[nb][3] += exp2_hw(fmaf(acc[nb][4 * g + 3], c, n.w));
-                }
-            }
-        }
-        if (t + 1 < ntiles) {
-            st.store(lds[(t + 1) & 1]);
-            if (threadIdx.x < QT) nlse[(t + 1) & 1][threadIdx.x] = -lse_next * kLog2e;
-        }
-        __syncthreads();
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (key < Lk) kf[kk].load(Kh + ((size_t)key * D + 16 * kk + 8 * half) * kE);
+        else kf[kk].zero();
     }
+    wait_vmcnt<L>();  // tile 0 landed (tile 1 may be in flight)
+    tile_barrier();
+
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    // acc[r] belongs to query row 8*(r/4) + 4*half + r%4 of its 32-row block;
+    // rows past L_q are zero in Q and -inf in -lse2, so they add nothing.
+    auto acc_rows = [&](const f32x16_t& acc, const float* nl, int r0, int nr) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        float v = (cs[nb][0] + cs[nb][1]) + (cs[nb][2] + cs[nb][3]);
-        v += __shfl_xor(v, 32, kWave);  // the other half of the queries of this key
-        const int key = key0 + 32 * nb;
-        if (lane < 32 && key < Lk) imp[(size_t)h * Lk + key] = v * inv_lq;
+        for (int r = r0; r < r0 + nr; ++r) {
+            const float p = exp2_hw(fmaf(acc[r], c, nl[8 * (r >> 2) + (r & 3)]));
+            if ((r & 3) == 0) c0 += p; else if ((r & 3) == 1) c1 += p; else if ((r & 3) == 2) c2 += p; else c3 += p;
+        }
+    };
+    auto step = [&](auto b, int t) {
+        constexpr int B = decltype(b)::value;
+        issue(Buf<(B + 2) % kNBuf>{}, t + 2);
+        const char* buf = lds(b);
+        const float* nl = nl_lds(b) + 4 * half;
+        if constexpr (QT == 64) {
+            f32x16_t a0, a1;
+            mfma_block<DT, D, QT>(a0, buf, 0, fo, kf, NoSlice{});
+            mfma_block<DT, D, QT>(a1, buf, 32, fo, kf, [&](int r0, int nr) { acc_rows(a0, nl, r0, nr); });
+            acc_rows(a1, nl + 32, 0, 16);
+        } else {
+            f32x16_t a0;
+            mfma_block<DT, D, QT>(a0, buf, 0, fo, kf, NoSlice{});
+            acc_rows(a0, nl, 0, 16);
+        }
+        wait_vmcnt<L>();
+        tile_barrier();
+    };
+    // Whole rounds of three tiles, then the tail: the loop's back edge then
+    // only follows a buffer-2 step, so the compiler sees on every path which
+    // loads the explicit waits have retired and adds no waits of its own.
+    int t = 0;
+    for (; t + 2 < ntiles; t += kNBuf) {
+        step(Buf<0>{}, t);
+        step(Buf<1>{}, t + 1);
+        step(Buf<2>{}, t + 2);
     }
+    if (t < ntiles) {
+        step(Buf<0>{}, t);
+        if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
+    }
+    wait_vmcnt<0>();
+    float v = (c0 + c1) + (c2 + c3);
+    v += __shfl_xor(v, 32, kWave);  // the other half of the queries of this key
+    if (lane < 32 && key < Lk) imp[(size_t)h * Lk + key] = v * inv_lq;
 }
 
 template <int DT, int D>
@@ -303,23 +510,25 @@ hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq,
 }
 
 template <int DT, int D>
-hipError_t colsum_launch(const void* Q, const void* K, const float* lse, float* imp, int H, int Lq, int Lk, float c,
+hipError_t colsum_launch(const void* Q, const void* K, const float* nlse2, float* imp, int H, int Lq, int Lk, float c,
                          hipStream_t s) {
     const int nkb = (Lk + kRowsPerBlock - 1) / kRowsPerBlock;
     const long long n_items = (long long)H * nkb;
     const int blocks = (int)((n_items + 7) / 8 * 8);
-    hipLaunchKernelGGL((imp_colsum_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, lse, imp, Lq, Lk, nkb,
-                       (int)n_items, c, 1.0f / (float)Lq);
+    hipLaunchKernelGGL((imp_colsum_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, nlse2, imp, Lq,
+                       imp_lq_pad(Lq), Lk, nkb, (int)n_items, c, 1.0f / (float)Lq);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int imp_lq_pad(int Lq) { return (Lq + 63) / 64 * 64; }
+
 ImpPlan imp_plan(int H, int Lq, int Lk, int dt) {
     const int kt = dt == kBF16 ? tile_rows<kBF16>() : tile_rows<kF32>();
     const long long blocks = (long long)H * ((Lq + kRowsPerBlock - 1) / kRowsPerBlock);
     const int max_split = (Lk + 4 * kt - 1) / (4 * kt);  // keep >= 4 tiles per split
-    int ns = (int)((2048 + blocks - 1) / blocks);         // ~8 blocks per CU: a short tail
+    int ns = (int)((2048 + blocks - 1) / blocks);         // several blocks per CU: a short tail
     if (ns > max_split) ns = max_split;
     if (ns < 1) ns = 1;
     int tiles = (Lk + kt - 1) / kt;
@@ -336,17 +545,26 @@ hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* p
                     : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s);
 }
 
-hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* lse, float* imp, int H,
+hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
                              int Lq, int Lk, float c, hipStream_t s) {
-    if (dt == kBF16) return d == 128 ? colsum_launch<kBF16, 128>(Q, K, lse, imp, H, Lq, Lk, c, s)
-                                     : colsum_launch<kBF16, 64>(Q, K, lse, imp, H, Lq, Lk, c, s);
-    return d == 128 ? colsum_launch<kF32, 128>(Q, K, lse, imp, H, Lq, Lk, c, s)
-                    : colsum_launch<kF32, 64>(Q, K, lse, imp, H, Lq, Lk, c, s);
+    if (dt == kBF16) return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s)
+                                     : colsum_launch<kBF16, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s);
+    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s)
+                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s);
 }
 
-hipError_t launch_imp_lse_merge(const float2* part, float* lse, int H, int Lq, int nsplit, hipStream_t s) {
-    hipLaunchKernelGGL(imp_lse_merge_kernel, dim3((Lq + kThreads - 1) / kThreads, H), dim3(kThreads), 0, s, part,
-                       lse, Lq, nsplit);
+hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,
+                                hipStream_t s) {
+    const int lq_pad = imp_lq_pad(Lq);
+    hipLaunchKernelGGL(imp_lse_merge_kernel, dim3((lq_pad + kSmallThreads - 1) / kSmallThreads, H),
+                       dim3(kSmallThreads), 0, s, part, lse, nlse2, Lq, lq_pad, nsplit);
+    return hipGetLastError();
+}
+
+hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipStream_t s) {
+    const int lq_pad = imp_lq_pad(Lq);
+    hipLaunchKernelGGL(imp_nlse2_kernel, dim3((lq_pad + kSmallThreads - 1) / kSmallThreads, H), dim3(kSmallThreads),
+                       0, s, lse, nlse2, Lq, lq_pad);
     return hipGetLastError();
 }
 

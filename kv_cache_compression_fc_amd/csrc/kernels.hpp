@@ -18,11 +18,18 @@ struct ImpPlan {
 ImpPlan imp_plan(int H, int Lq, int Lk, int dt);
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
                           int Lk, const ImpPlan& plan, float c, hipStream_t s);
-// Pass 2 from the natural-log lse [H][Lq].
-hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* lse, float* imp, int H,
+// Queries padded to whole pass-2 tiles.
+int imp_lq_pad(int Lq);
+// Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled
+// logits, negated, padded with -inf).
+hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
                              int Lq, int Lk, float c, hipStream_t s);
-// Natural-log lse [H][Lq] from the pass-1 partials.
-hipError_t launch_imp_lse_merge(const float2* part, float* lse, int H, int Lq, int nsplit, hipStream_t s);
+// From the pass-1 partials: the natural-log lse [H][Lq] and/or -lse2 (either
+// may be nullptr).
+hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,
+                                hipStream_t s);
+// -lse2 from a natural-log lse.
+hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipStream_t s);
 
 // ---- redundancy -------------------------------------------------------------
 // Blocks per head of the two redundancy passes.
@@ -57,9 +64,11 @@ hipError_t launch_sel_keys_from_imp(const float* imp, const float* r, const floa
 hipError_t launch_sel_keys_from_scores(const float* scores, const SelBuffers& b, int H, int L,
                                        hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
-// Radix refinement, counting, compaction (+ optional K/V gather).
-hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int dt, int d, const void* K,
-                             const void* V, void* K_out, void* V_out, int32_t* idx_out, hipStream_t s);
+// Radix refinement, counting and compaction into idx_out [H][Bp].
+hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int32_t* idx_out, hipStream_t s);
+// K_out[h][b] = K[h][idx[h][b]], V likewise.
+hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
+                         void* K_out, void* V_out, hipStream_t s);
 
 // ---- chunk relative L1 ------------------------------------------------------
 constexpr int kMaxChunks = 128;

@@ -16,6 +16,7 @@ namespace fc {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRowsInFlight = 4;  // rows each lane group loads before reducing
 
 // Thread layout for one row of D elements of type DT: 16 bytes per lane.
 template <int DT, int D>
@@ -70,16 +71,27 @@ __global__ __launch_bounds__(kThreads) void red_norm_sum_kernel(const void* __re
     float u[RL::kVec];
 #pragma unroll
     for (int v = 0; v < RL::kVec; ++v) u[v] = 0.f;
-    for (int row = r0 + g; row < r1; row += RL::kRpi) {
-        float x[RL::kVec];
-        load_vec<DT>(Kh + ((size_t)row * D + e * RL::kVec) * kE, x);
-        float n2 = 0.f;
+    for (int row = r0 + g; row < r1; row += kRowsInFlight * RL::kRpi) {
+        float x[kRowsInFlight][RL::kVec];
 #pragma unroll
-        for (int v = 0; v < RL::kVec; ++v) n2 = fmaf(x[v], x[v], n2);
-        n2 = group_sum<RL::kTpr>(n2);
-        const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int rr = row + i * RL::kRpi;
+            if (rr < r1) load_vec<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
+            else {
 #pragma unroll
-        for (int v = 0; v < RL::kVec; ++v) u[v] = fmaf(x[v], inv, u[v]);
+                for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;  // contributes nothing to u
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            float n2 = 0.f;
+#pragma unroll
+            for (int v = 0; v < RL::kVec; ++v) n2 = fmaf(x[i][v], x[i][v], n2);
+            n2 = group_sum<RL::kTpr>(n2);
+            const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+#pragma unroll
+            for (int v = 0; v < RL::kVec; ++v) u[v] = fmaf(x[i][v], inv, u[v]);
+        }
     }
 #pragma unroll
     for (int v = 0; v < RL::kVec; ++v) red[g][e * RL::kVec + v] = u[v];
@@ -137,22 +149,34 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
     const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
     const float inv_lk = 1.0f / (float)Lk;
     float m = -1e30f, s = 0.f;  // base-2 running stats of r * log2e
-    for (int row = r0 + g; row < r1; row += RL::kRpi) {
-        float x[RL::kVec];
-        load_vec<DT>(Kh + ((size_t)row * D + e * RL::kVec) * kE, x);
-        float dot = 0.f, n2 = 0.f;
+    for (int row = r0 + g; row < r1; row += kRowsInFlight * RL::kRpi) {
+        float x[kRowsInFlight][RL::kVec];
 #pragma unroll
-        for (int v = 0; v < RL::kVec; ++v) {
-            dot = fmaf(x[v], u[v], dot);
-            n2 = fmaf(x[v], x[v], n2);
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int rr = row + i * RL::kRpi;
+            if (rr < r1) load_vec<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
+            else {
+#pragma unroll
+                for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;
+            }
         }
-        dot = group_sum<RL::kTpr>(dot);
-        n2 = group_sum<RL::kTpr>(n2);
-        const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
-        const float rj = (dot * inv - n2 * inv * inv) * inv_lk;
-        if (e == 0) {
-            r[(size_t)h * Lk + row] = rj;
-            lse2_merge(m, s, rj * kLog2e, 1.0f);
+#pragma unroll
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int rr = row + i * RL::kRpi;
+            float dot = 0.f, n2 = 0.f;
+#pragma unroll
+            for (int v = 0; v < RL::kVec; ++v) {
+                dot = fmaf(x[i][v], u[v], dot);
+                n2 = fmaf(x[i][v], x[i][v], n2);
+            }
+            dot = group_sum<RL::kTpr>(dot);
+            n2 = group_sum<RL::kTpr>(n2);
+            const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+            const float rj = (dot * inv - n2 * inv * inv) * inv_lk;
+            if (e == 0 && rr < r1) {
+                r[(size_t)h * Lk + rr] = rj;
+                lse2_merge(m, s, rj * kLog2e, 1.0f);
+            }
         }
     }
     block_softmax_stats(m, s, red_part + (size_t)h * nblk + blk);

@@ -11,9 +11,9 @@
 // LDS histograms merged with integer atomics) finds the B'-th largest key T
 // and the number q of keys equal to T that fit, and a compaction keeps every
 // key > T plus the first q keys == T in token order (ties go to the lower
-// index).  Kept tokens are written in ascending token order; their K and V
-// rows are copied in the same pass.  Integer atomics only, so the result is
-// deterministic.
+// index).  Kept tokens are written in ascending token order, and a gather
+// kernel with one block per 64 kept rows copies their K and V rows.  Integer
+// atomics only, so the result is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -250,29 +250,12 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const uint32_t* __r
     }
 }
 
-template <int DT, int D>
-__device__ __forceinline__ void copy_rows(const void* __restrict__ src, void* __restrict__ dst,
-                                          const int* rows, int n) {
-    constexpr int kRowBytes = D * Elem<DT>::kBytes;
-    constexpr int kTpr = kRowBytes / 16;     // lanes per row
-    constexpr int kRpi = kThreads / kTpr;    // rows per step
-    const int g = threadIdx.x / kTpr, e = threadIdx.x % kTpr;
-    const char* s = static_cast<const char*>(src);
-    char* d = static_cast<char*>(dst);
-    for (int i = g; i < n; i += kRpi) {
-        const uint4 v = *reinterpret_cast<const uint4*>(s + (size_t)rows[i] * kRowBytes + e * 16);
-        *reinterpret_cast<uint4*>(d + (size_t)i * kRowBytes + e * 16) = v;
-    }
-}
-
-// Compaction in token order (+ K/V row copy when K != nullptr).
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void sel_compact_kernel(
-    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ counts, const uint32_t* __restrict__ state,
-    int L, int Bp, int32_t* __restrict__ idx_out, const void* __restrict__ K, const void* __restrict__ V,
-    void* __restrict__ K_out, void* __restrict__ V_out) {
+// Compaction in token order: every kept token's index at its output slot.
+__global__ __launch_bounds__(kThreads) void sel_compact_kernel(const uint32_t* __restrict__ keys,
+                                                               const uint32_t* __restrict__ counts,
+                                                               const uint32_t* __restrict__ state, int L, int Bp,
+                                                               int32_t* __restrict__ idx_out) {
     __shared__ uint32_t scan_lds[4];
-    __shared__ int sel_rows[kSelTile];
     __shared__ uint32_t base_lds[2];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
     const uint32_t T = state[2 * h + 0], q = state[2 * h + 1];
@@ -313,23 +296,58 @@ __global__ __launch_bounds__(kThreads) void sel_compact_kernel(
         if (s) { sel_mask |= 1u << i; ++nsel; }
     }
     uint32_t tsel;
-    uint32_t pos = block256_exclusive_scan(nsel, scan_lds, &tsel);
+    uint32_t pos = out_base + block256_exclusive_scan(nsel, scan_lds, &tsel);
     int32_t* idx_h = idx_out + (size_t)h * Bp;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         if (sel_mask & (1u << i)) {
-            if (out_base + pos < (uint32_t)Bp) idx_h[out_base + pos] = j0 + i;  // always true when counts agree
-            sel_rows[pos] = j0 + i;
+            if (pos < (uint32_t)Bp) idx_h[pos] = j0 + i;  // always true when the counts agree
             ++pos;
         }
     }
-    if (K == nullptr) return;
-    __syncthreads();
-    const int nrows = out_base >= (uint32_t)Bp ? 0 : (int)min(tsel, (uint32_t)Bp - out_base);
-    const size_t in_off = (size_t)h * L * D * Elem<DT>::kBytes;
-    const size_t out_off = ((size_t)h * Bp + min(out_base, (uint32_t)Bp)) * D * Elem<DT>::kBytes;
-    copy_rows<DT, D>(static_cast<const char*>(K) + in_off, static_cast<char*>(K_out) + out_off, sel_rows, nrows);
-    copy_rows<DT, D>(static_cast<const char*>(V) + in_off, static_cast<char*>(V_out) + out_off, sel_rows, nrows);
+}
+
+// K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
+// kRowBytes/16 lanes, kGatherRows output rows per block.
+constexpr int kGatherRows = 64;
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __restrict__ idx, int L, int Bp,
+                                                               const void* __restrict__ K, const void* __restrict__ V,
+                                                               void* __restrict__ K_out, void* __restrict__ V_out) {
+    constexpr int kRowBytes = D * Elem<DT>::kBytes;
+    constexpr int kTpr = kRowBytes / 16;     // lanes per row
+    constexpr int kRpi = kThreads / kTpr;    // rows per step
+    constexpr int kSteps = kGatherRows / kRpi;
+    const int h = blockIdx.y;
+    const int b0 = blockIdx.x * kGatherRows + threadIdx.x / kTpr;
+    const int e = threadIdx.x % kTpr;
+    const char* Ks = static_cast<const char*>(K) + (size_t)h * L * kRowBytes + e * 16;
+    const char* Vs = static_cast<const char*>(V) + (size_t)h * L * kRowBytes + e * 16;
+    char* Kd = static_cast<char*>(K_out) + (size_t)h * Bp * kRowBytes + e * 16;
+    char* Vd = static_cast<char*>(V_out) + (size_t)h * Bp * kRowBytes + e * 16;
+    int j[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+        const int b = b0 + i * kRpi;
+        j[i] = b < Bp ? idx[(size_t)h * Bp + b] : -1;
+    }
+    uint4 kv[kSteps], vv[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+        if ((unsigned)j[i] < (unsigned)L) {
+            kv[i] = *reinterpret_cast<const uint4*>(Ks + (size_t)j[i] * kRowBytes);
+            vv[i] = *reinterpret_cast<const uint4*>(Vs + (size_t)j[i] * kRowBytes);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+        if ((unsigned)j[i] < (unsigned)L) {
+            const size_t b = (size_t)(b0 + i * kRpi);
+            *reinterpret_cast<uint4*>(Kd + b * kRowBytes) = kv[i];
+            *reinterpret_cast<uint4*>(Vd + b * kRowBytes) = vv[i];
+        }
+    }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
@@ -338,10 +356,10 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
 }
 
 template <int DT, int D>
-hipError_t compact_launch(const SelBuffers& b, int H, int L, int Bp, const void* K, const void* V, void* K_out,
-                          void* V_out, int32_t* idx_out, hipStream_t s) {
-    hipLaunchKernelGGL((sel_compact_kernel<DT, D>), dim3(sel_nblk(L), H), dim3(kThreads), 0, s, b.keys, b.counts,
-                       b.state, L, Bp, idx_out, K, V, K_out, V_out);
+hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
+                         void* V_out, hipStream_t s) {
+    const dim3 grid((Bp + kGatherRows - 1) / kGatherRows, H);
+    hipLaunchKernelGGL((gather_rows_kernel<DT, D>), grid, dim3(kThreads), 0, s, idx, L, Bp, K, V, K_out, V_out);
     return hipGetLastError();
 }
 
@@ -368,19 +386,22 @@ hipError_t launch_sel_keys_from_scores(const float* scores, const SelBuffers& b,
     return hipGetLastError();
 }
 
-hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int dt, int d, const void* K,
-                             const void* V, void* K_out, void* V_out, int32_t* idx_out, hipStream_t s) {
+hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int32_t* idx_out, hipStream_t s) {
     const dim3 grid(sel_nblk(L), H);
     hipLaunchKernelGGL(sel_refine_kernel<1>, grid, dim3(kThreads), 0, s, b.keys, b.hist, L, Bp);
     hipLaunchKernelGGL(sel_refine_kernel<2>, grid, dim3(kThreads), 0, s, b.keys, b.hist, L, Bp);
     hipLaunchKernelGGL(sel_count_kernel, grid, dim3(kThreads), 0, s, b.keys, b.hist, b.counts, b.state, L, Bp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_compact_kernel, grid, dim3(kThreads), 0, s, b.keys, b.counts, b.state, L, Bp, idx_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
+                         void* K_out, void* V_out, hipStream_t s) {
     if (dt == kBF16)
-        return d == 128 ? compact_launch<kBF16, 128>(b, H, L, Bp, K, V, K_out, V_out, idx_out, s)
-                        : compact_launch<kBF16, 64>(b, H, L, Bp, K, V, K_out, V_out, idx_out, s);
-    return d == 128 ? compact_launch<kF32, 128>(b, H, L, Bp, K, V, K_out, V_out, idx_out, s)
-                    : compact_launch<kF32, 64>(b, H, L, Bp, K, V, K_out, V_out, idx_out, s);
+        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, s)
+                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, s);
+    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, s)
+                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, s);
 }
 
 }  // namespace fc

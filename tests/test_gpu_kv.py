@@ -200,3 +200,31 @@ def test_importance_two_stages(fc, dtype, d, H, Lq, Lk):
     # an absolute lse error e is a relative error e on every exp(s - lse)
     assert float(np.max(np.abs(lse.cpu().double().numpy() - want_lse))) <= 1e-4
     assert parity.max_rel_err(imp.cpu().numpy(), oracle.importance(Q, K, 1 / math.sqrt(d))) <= parity.REL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_importance_wide_logit_range(fc, dtype):
+    # a later key scores ~150 binary orders above the first keys of its range,
+    # which the fixed shift of pass 1 cannot hold: the exact path must take over
+    H, Lq, Lk, d = 2, 70, 700, 64
+    rng = np.random.default_rng(13)
+    Q = rng.standard_normal((H, Lq, d)).astype(np.float32)
+    K = 0.01 * rng.standard_normal((H, Lk, d)).astype(np.float32)
+    Q[:, :, 0] = 10.0
+    K[0, 600, 0] = 10.0          # logit 100 (scale 1) against ~0 for the rest
+    K[1, 333, 0] = -10.0         # and a very negative one
+    Qt, Kt = torch.from_numpy(Q), torch.from_numpy(K)
+    if dtype == "bf16":
+        Qt, Kt = Qt.to(torch.bfloat16), Kt.to(torch.bfloat16)
+    say(f"case: importance with a 100-nat logit spread ({dtype})")
+    imp = fc.fc_kv_importance(Qt.to(DEV), Kt.to(DEV), softmax_scale=1.0)
+    lse = fc.fc_kv_importance_lse(Qt.to(DEV), Kt.to(DEV), softmax_scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(imp).all() and torch.isfinite(lse).all()
+    want = oracle.importance(Qt, Kt, 1.0)
+    # relative error on the entries that carry the mass; tiny ones absolutely
+    got = imp.cpu().double().numpy()
+    big = want > 1e-30
+    assert float(np.max(np.abs(got[big] - want[big]) / want[big])) <= parity.REL or \
+        float(np.max(np.abs(got - want))) <= 1e-6
+    np.testing.assert_allclose(lse.cpu().double().numpy(), oracle.lse(Qt, Kt, 1.0), rtol=0, atol=1e-3)
