@@ -83,19 +83,32 @@ def time_graph(fn, reps: int):
         return time_events(fn, reps), "eager"
 
 
-def cpu_baseline(cfg, n_heads: int):
-    """The oracle (never tuned) on n_heads heads of the same workload."""
+def cpu_baseline(cfg, ccfg, min_seconds: float):
+    """The oracle (never tuned) on whole steps of the same workload: all heads
+    of the KV compression and the decision for every chunk, repeated until
+    about min_seconds of host time have passed."""
     import oracle
     from kv_cache_compression_fc_amd import synth
-    heads = list(range(n_heads))
-    Q, K, V = synth.kv_inputs(cfg, seed=0, heads=heads)
-    t0 = time.perf_counter()
-    oracle.kv_compress(Q, K, V, cfg.B, cfg.lam[0], cfg.w)
-    dt = time.perf_counter() - t0
-    return {"value": n_heads * cfg.Lk / dt, "unit": "token-heads/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"{n_heads} of {cfg.H} heads of the MAGI-like workload at full L_q={cfg.Lq}, L_k={cfg.Lk}: "
-                      "importance, redundancy, pool, score, top-B and gather in fp64 (C + OpenMP, numpy)"}
+    Q, K, V = synth.kv_inputs(cfg, seed=0)
+    tr = synth.ChunkTrajectory(ccfg, seed=0)
+    xt, xtm1, steps = tr.pair(ccfg.n_chunks - 1)
+    offs = [i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)]
+    f = [0.0] * ccfg.n_chunks
+    reps, t_total = 0, 0.0
+    while reps == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        oracle.kv_compress(Q, K, V, cfg.B, cfg.lam[0], cfg.w)
+        l1 = oracle.chunk_l1_rel(xt, xtm1, offs)
+        for i, n in enumerate(steps):
+            if n >= 0:
+                _, f[i] = oracle.decide(n, f[i], l1[i], ccfg.m, ccfg.eps[0])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": cfg.H * cfg.Lk * reps / t_total, "unit": "token-heads/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": t_total,
+            "sample": f"{reps} whole step(s) of the same workload: fp64 compression of all {cfg.H} heads "
+                      f"(L_q={cfg.Lq}, L_k={cfg.Lk}, C + OpenMP importance, numpy rest) and the relative-L1 "
+                      f"decision of {ccfg.n_chunks} chunks (numpy)"}
 
 
 def main() -> int:
@@ -104,7 +117,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--cpu-heads", type=int, default=6)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time of the CPU-baseline (oracle) leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
@@ -244,8 +258,8 @@ def main() -> int:
         "stages": stages,
     }
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_heads} heads")
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+        log("cpu baseline: oracle on whole steps")
+        result["cpu_baseline"] = cpu_baseline(cfg, ccfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

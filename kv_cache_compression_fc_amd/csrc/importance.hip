@@ -155,15 +155,16 @@ __device__ __forceinline__ int xcd_item(int per_xcd) {
 #define FC_SB() __builtin_amdgcn_sched_barrier(0)
 
 // acc = (32 streamed rows starting at row r0 of the tile) x (register operand):
-// a 32x32 fp32 tile.  Fragment reads run half a block ahead of the MFMAs
-// that consume them; with `slice` each MFMA
-// is followed, in a fixed order, by vector work on another block (16/NKK of
-// its rows), so that work runs in the MFMA shadow.
-template <int DT, int D, int ROWS, typename Slice>
+// a 32x32 fp32 tile; with kRegRows the register operand supplies the rows of
+// acc and the streamed rows its columns instead.  Fragment reads run two
+// MFMAs ahead of the ones that consume them; with `slice` each MFMA is
+// followed, in a fixed order, by vector work on another block (16/NKK of its
+// rows), so that work runs in the MFMA shadow.
+template <int DT, int D, int ROWS, bool kRegRows = false, typename Slice>
 __device__ __forceinline__ void mfma_block(f32x16_t& acc, const char* buf, int r0, const FragOffsets<DT, D, ROWS>& fo,
                                            const Frag8<DT> (&b)[D / 16], Slice&& slice) {
     constexpr int NKK = D / 16;
-    constexpr int P = NKK / 2;  // fragment reads kept ahead of the MFMA that uses them
+    constexpr int P = NKK >= 4 ? 2 : 1;  // fragment reads kept ahead of the MFMA that uses them
     const char* blk = buf + r0 * SwizzledTile<DT, D, ROWS>::kRowBytes;
     Frag8<DT> a[NKK];
 #pragma unroll
@@ -173,7 +174,8 @@ __device__ __forceinline__ void mfma_block(f32x16_t& acc, const char* buf, int r
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         if (kk + P < NKK) load_frag<DT, D, ROWS>(a[kk + P], blk, fo, kk + P);
-        mfma16(acc, a[kk], b[kk]);
+        if constexpr (kRegRows) mfma16(acc, b[kk], a[kk]);
+        else mfma16(acc, a[kk], b[kk]);
         FC_SB();
         slice(kk * (16 / NKK), 16 / NKK);
         FC_SB();
@@ -270,6 +272,14 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
     };
     // Tile t is read from buffer t % 3; tile t+2 goes into the buffer tile t-1
     // used, which every wave has left (barrier at the end of step t-1).
+    // The exponentials of each 32-key block run in the MFMA shadow of the
+    // next block: block 1 of tile t is finished during block 0 of tile t+1
+    // (`carry`), so every wave alternates MFMA and vector work throughout
+    // instead of all waves of the workgroup doing one, then the other, between
+    // barriers.  carry starts at -inf (adds 0).
+    f32x16_t carry;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) carry[r] = -INFINITY;
     auto step = [&](auto b, int t) {
         constexpr int B = decltype(b)::value;
         // Past the last tile the offset lies outside the resource: the load
@@ -279,22 +289,20 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
                     lds(Buf<(B + 2) % kNBuf>{}), wave, lane);
         const char* buf = lds(b);
         const int valid = nkeys - t * KT;  // rows of this tile inside the range
+        f32x16_t a0;
+        mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, [&](int r0, int nr) { acc_rows(carry, r0, nr); });
+        if (valid < 32) mask_rows(a0, valid, half);
         if constexpr (KT == 64) {
-            f32x16_t a0, a1;
-            mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, NoSlice{});
-            if (valid < 32) mask_rows(a0, valid, half);
             if (valid > 32) {
-                mfma_block<DT, D, KT>(a1, buf, 32, fo, qf, [&](int r0, int nr) { acc_rows(a0, r0, nr); });
-                if (valid < 64) mask_rows(a1, valid - 32, half);
-                acc_rows(a1, 0, 16);
+                mfma_block<DT, D, KT>(carry, buf, 32, fo, qf, [&](int r0, int nr) { acc_rows(a0, r0, nr); });
+                if (valid < 64) mask_rows(carry, valid - 32, half);
             } else {
                 acc_rows(a0, 0, 16);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) carry[r] = -INFINITY;
             }
         } else {
-            f32x16_t a0;
-            mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, NoSlice{});
-            if (valid < 32) mask_rows(a0, valid, half);
-            acc_rows(a0, 0, 16);
+            carry = a0;
         }
         wait_vmcnt<L>();  // tile t+1 landed, tile t+2 may be in flight
         tile_barrier();
@@ -313,6 +321,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
     }
     wait_vmcnt<0>();
+    acc_rows(carry, 0, 16);
 
     float m = -nm, tot = (s0 + s1) + (s2 + s3);
     if (__syncthreads_or(!(tot < 0x1p100f))) {  // overflow (or NaN) under the fixed shift
@@ -441,7 +450,10 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
     issue(Buf<0>{}, 0);
     issue(Buf<1>{}, 1);  // (out of range when there is one tile)
 
-    // K^T fragments (B operand): key, depth 16*kk + 8*half .. +8.
+    // K fragments, the register operand: key (lane%32 of the wave's 32),
+    // depth 16*kk + 8*half .. +8.  They supply the rows of every product, so
+    // acc[r] is key row 8*(r/4) + 4*half + r%4 and query lane%32 of the
+    // streamed 32-row block, and a query's -lse2 is one value per lane.
     Frag8<DT> kf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -451,30 +463,35 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
     wait_vmcnt<L>();  // tile 0 landed (tile 1 may be in flight)
     tile_barrier();
 
-    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
-    // acc[r] belongs to query row 8*(r/4) + 4*half + r%4 of its 32-row block;
-    // rows past L_q are zero in Q and -inf in -lse2, so they add nothing.
-    auto acc_rows = [&](const f32x16_t& acc, const float* nl, int r0, int nr) {
+    // Per key row r: this lane's share of sum_i exp2(x_ij - lse2_i).  Rows
+    // past L_q are zero in Q and -inf in -lse2, so they add nothing.
+    float cs[16];
 #pragma unroll
-        for (int r = r0; r < r0 + nr; ++r) {
-            const float p = exp2_hw(fmaf(acc[r], c, nl[8 * (r >> 2) + (r & 3)]));
-            if ((r & 3) == 0) c0 += p; else if ((r & 3) == 1) c1 += p; else if ((r & 3) == 2) c2 += p; else c3 += p;
-        }
+    for (int r = 0; r < 16; ++r) cs[r] = 0.f;
+    auto acc_rows = [&](const f32x16_t& acc, float nl, int r0, int nr) {
+#pragma unroll
+        for (int r = r0; r < r0 + nr; ++r) cs[r] += exp2_hw(fmaf(acc[r], c, nl));
     };
+    // As in imp_lse_kernel, the second block of tile t is finished in the MFMA
+    // shadow of the first block of tile t+1 (carry, with its -lse2 value).
+    f32x16_t carry;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) carry[r] = 0.f;
+    float nl_carry = -INFINITY;  // adds 0
     auto step = [&](auto b, int t) {
         constexpr int B = decltype(b)::value;
         issue(Buf<(B + 2) % kNBuf>{}, t + 2);
         const char* buf = lds(b);
-        const float* nl = nl_lds(b) + 4 * half;
+        const float nl_a = nl_lds(b)[lane & 31];
+        f32x16_t a0;
+        mfma_block<DT, D, QT, true>(a0, buf, 0, fo, kf, [&](int r0, int nr) { acc_rows(carry, nl_carry, r0, nr); });
         if constexpr (QT == 64) {
-            f32x16_t a0, a1;
-            mfma_block<DT, D, QT>(a0, buf, 0, fo, kf, NoSlice{});
-            mfma_block<DT, D, QT>(a1, buf, 32, fo, kf, [&](int r0, int nr) { acc_rows(a0, nl, r0, nr); });
-            acc_rows(a1, nl + 32, 0, 16);
+            const float nl_b = nl_lds(b)[32 + (lane & 31)];
+            mfma_block<DT, D, QT, true>(carry, buf, 32, fo, kf, [&](int r0, int nr) { acc_rows(a0, nl_a, r0, nr); });
+            nl_carry = nl_b;
         } else {
-            f32x16_t a0;
-            mfma_block<DT, D, QT>(a0, buf, 0, fo, kf, NoSlice{});
-            acc_rows(a0, nl, 0, 16);
+            carry = a0;
+            nl_carry = nl_a;
         }
         wait_vmcnt<L>();
         tile_barrier();
@@ -493,9 +510,20 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
     }
     wait_vmcnt<0>();
-    float v = (c0 + c1) + (c2 + c3);
-    v += __shfl_xor(v, 32, kWave);  // the other half of the queries of this key
-    if (lane < 32 && key < Lk) imp[(size_t)h * Lk + key] = v * inv_lq;
+    acc_rows(carry, nl_carry, 0, 16);
+
+    // Sum each key row over the 32 query lanes of its half (fixed butterfly
+    // order), then lane r of each half writes row r.
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float x = cs[r];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+        if ((lane & 31) == r) v = x;
+    }
+    const int kr = kblk * kRowsPerBlock + wave * 32 + 8 * ((lane & 15) >> 2) + 4 * half + (lane & 3);
+    if ((lane & 31) < 16 && kr < Lk) imp[(size_t)h * Lk + kr] = v * inv_lq;
 }
 
 template <int DT, int D>
