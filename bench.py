@@ -12,7 +12,7 @@ already resident in HBM:
 
 Prints one JSON line.  `value` is clean-KV token-heads scored and selected per
 second over whole steps (the chunk decision included).  The dominant kernel
-(importance pass 2) is timed on its own with HIP events on the stream it runs
+(importance pass 1) is timed on its own with HIP events on the stream it runs
 on, for the roofline entry; the oracle is timed on the host cores on a bounded
 sample for the CPU baseline.
 """
@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "clean KV tokens scored+selected/sec/head; L1 GB/s; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "imp_colsum_magi_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "imp_lse_magi_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_compression_fc_amd", "csrc", "importance.hip")
 
 
@@ -211,11 +211,11 @@ def main() -> int:
     red_bytes = H * Lk * (d * 2 + 4)              # read K once, write r
     sel_bytes = 8 * H * Lk + 4 * H * Bp + 2 * 2 * H * Bp * d * 2   # imp + r, idx, K/V rows read + written
     l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
-    colsum_tflops = mfma_flops / (t_colsum * 1e-3) / 1e12
+    lse_tflops = mfma_flops / (t_lse * 1e-3) / 1e12
     stages = {
-        "importance_lse_ms": t_lse, "importance_lse_tflops": mfma_flops / (t_lse * 1e-3) / 1e12,
-        "importance_colsum_ms": t_colsum, "importance_colsum_tflops": colsum_tflops,
-        "redundancy_ms": t_red, "redundancy_gbps": red_bytes / (t_red * 1e-3) / 1e9,
+        "importance_lse_ms": t_lse, "importance_lse_tflops": lse_tflops,
+        "importance_colsum_ms": t_colsum, "importance_colsum_tflops": mfma_flops / (t_colsum * 1e-3) / 1e12,
+        "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "timing": f"events; redundancy {how_red}, select {how_sel}",
@@ -250,10 +250,10 @@ def main() -> int:
         "tokens_per_s_per_head": Lk / (ms_per_step * 1e-3),
         "l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "imp_colsum_kernel<bf16,128> (importance pass 2)",
-            "bound": "mfma", "achieved": colsum_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": colsum_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-            "avg_launch_ms": t_colsum, "algorithmic_per_launch": mfma_flops,
+            "kernel": "imp_lse_kernel<bf16,128> (importance pass 1)",
+            "bound": "mfma", "achieved": lse_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": lse_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "avg_launch_ms": t_lse, "algorithmic_per_launch": mfma_flops,
         },
         "stages": stages,
     }

@@ -19,8 +19,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // ---- KV compression -------------------------------------------------------------------
 struct KvLayout {
     ImpPlan plan;
-    int nbu, nbr, nbs;
-    size_t part, nlse2, imp, r, u_part, red_part, keys, hist, counts, state, total;
+    int nbu, nbr;
+    int nkb;  // importance pass-2 workgroups per head (redundancy softmax partials of the fused path)
+    size_t part, nlse2, imp, r, u_part, u, red_part, keys, total;
 };
 
 fc_status check_kv(const fc_kv_params* p) {
@@ -45,7 +46,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.plan = imp_plan(p->H, p->L_q, p->L_k, dt);
     L.nbu = red_nbu(p->L_k);
     L.nbr = red_nbr(p->L_k);
-    L.nbs = sel_nblk(p->L_k);
+    L.nkb = imp_colsum_blocks(p->L_k);
     const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
@@ -53,22 +54,15 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.imp = o;      o = align_up(o + H * Lk * sizeof(float));
     L.r = o;        o = align_up(o + H * Lk * sizeof(float));
     L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
-    L.red_part = o; o = align_up(o + H * L.nbr * sizeof(float2));
+    L.u = o;        o = align_up(o + H * (size_t)p->d * sizeof(float));
+    L.red_part = o; o = align_up(o + H * (size_t)(L.nbr > L.nkb ? L.nbr : L.nkb) * sizeof(float2));
     L.keys = o;     o = align_up(o + H * Lk * sizeof(uint32_t));
-    L.hist = o;     o = align_up(o + H * kHistWordsPerHead * sizeof(uint32_t));
-    L.counts = o;   o = align_up(o + H * L.nbs * 2 * sizeof(uint32_t));
-    L.state = o;    o = align_up(o + H * 2 * sizeof(uint32_t));
     L.total = o;
     return L;
 }
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
-
-SelBuffers sel_buffers(void* ws, const KvLayout& L) {
-    return SelBuffers{at<uint32_t>(ws, L.keys), at<uint32_t>(ws, L.hist), at<uint32_t>(ws, L.counts),
-                      at<uint32_t>(ws, L.state)};
-}
 
 float log2_scale(const fc_kv_params* p) {
     const float scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->d);
@@ -83,15 +77,21 @@ fc_status hip_status(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_HIP
         if (e_ != hipSuccess) return FC_ERR_HIP;     \
     } while (0)
 
+// Importance (two passes).  With `r` the second pass also produces the
+// redundancy of the keys it holds (u from the partials red_norm_sum left in
+// the workspace) and the softmax partials of r, one per workgroup.
 fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp,
-                         void* ws, hipStream_t s) {
+                         void* ws, hipStream_t s, float* r = nullptr) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const float c = log2_scale(p);
     float2* part = at<float2>(ws, L.part);
     float* nlse2 = at<float>(ws, L.nlse2);
+    float* u = r ? at<float>(ws, L.u) : nullptr;
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
-    FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp, p->H, p->L_q, p->L_k, c, s));
+    FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s,
+                                r ? at<float>(ws, L.u_part) : nullptr, L.nbu, u, p->d));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp, p->H, p->L_q, p->L_k, c, s, u, r,
+                             r ? at<float2>(ws, L.red_part) : nullptr));
     return FC_OK;
 }
 
@@ -157,17 +157,14 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
     float* imp = at<float>(ws, L.imp);
     float* r = at<float>(ws, L.r);
     float2* red_part = at<float2>(ws, L.red_part);
-    const SelBuffers sb = sel_buffers(ws, L);
-    // redundancy (also clears the selection histograms)
-    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, sb.hist, kHistWordsPerHead, s));
-    FC_TRY(launch_red_dot(dt, p->d, K, at<float>(ws, L.u_part), r, red_part, p->H, p->L_k, s));
-    // importance
-    st = run_importance(p, L, Q, K, imp, ws, s);
+    // redundancy pass A: partial sums of the normalised keys
+    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, s));
+    // importance; its second pass also forms r and the softmax partials of r
+    st = run_importance(p, L, Q, K, imp, ws, s, r);
     if (st != FC_OK) return st;
     // pool + score + top-B + gather
-    FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
-                                    red_out, sb, p->H, p->L_k, s));
-    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, idx_out, s));
+    FC_TRY(launch_sel_head(imp, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
+                           at<uint32_t>(ws, L.keys), p->H, p->L_k, Bp, idx_out, s));
     FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
 }
@@ -221,7 +218,7 @@ fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, v
     if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
-    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(workspace, L.u_part), p->H, p->L_k, nullptr, 0, s));
+    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(workspace, L.u_part), p->H, p->L_k, s));
     FC_TRY(launch_red_dot(dt, p->d, K, at<float>(workspace, L.u_part), r_out, at<float2>(workspace, L.red_part),
                           p->H, p->L_k, s));
     return FC_OK;
@@ -242,24 +239,17 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
-    const SelBuffers sb = sel_buffers(workspace, L);
     float2* red_part = at<float2>(workspace, L.red_part);
-    FC_TRY(launch_red_stats(r, red_part, p->H, p->L_k, sb.hist, kHistWordsPerHead, s));
-    FC_TRY(launch_sel_keys_from_imp(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out,
-                                    red_out, sb, p->H, p->L_k, s));
-    FC_TRY(launch_sel_finish(sb, p->H, p->L_k, Bp, idx_out, s));
+    FC_TRY(launch_red_stats(r, red_part, p->H, p->L_k, s));
+    FC_TRY(launch_sel_head(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
+                           at<uint32_t>(workspace, L.keys), p->H, p->L_k, Bp, idx_out, s));
     if (gather) FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
 }
 
 size_t fc_topb_select_workspace_bytes(int32_t H, int32_t L) {
     if (H < 1 || L < 1 || H > 65535) return 0;
-    const size_t h = (size_t)H;
-    size_t o = align_up(h * (size_t)L * sizeof(uint32_t));             // keys
-    o += align_up(h * kHistWordsPerHead * sizeof(uint32_t));            // hist
-    o += align_up(h * sel_nblk(L) * 2 * sizeof(uint32_t));              // counts
-    o += align_up(h * 2 * sizeof(uint32_t));                            // state
-    return o;
+    return align_up((size_t)H * (size_t)L * sizeof(uint32_t));  // keys
 }
 
 fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, int32_t* idx_out, void* workspace,
@@ -268,18 +258,9 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
     if (H > 65535) return FC_ERR_UNSUPPORTED;
     const size_t need = fc_topb_select_workspace_bytes(H, L);
     if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t h = (size_t)H;
-    size_t o = 0;
-    SelBuffers sb;
-    sb.keys = at<uint32_t>(workspace, o);   o += align_up(h * (size_t)L * sizeof(uint32_t));
-    sb.hist = at<uint32_t>(workspace, o);   o += align_up(h * kHistWordsPerHead * sizeof(uint32_t));
-    sb.counts = at<uint32_t>(workspace, o); o += align_up(h * sel_nblk(L) * 2 * sizeof(uint32_t));
-    sb.state = at<uint32_t>(workspace, o);
     const int Bp = B < L ? B : L;
-    FC_TRY(launch_zero_u32(sb.hist, h * kHistWordsPerHead, s));
-    FC_TRY(launch_sel_keys_from_scores(scores, sb, H, L, s));
-    FC_TRY(launch_sel_finish(sb, H, L, Bp, idx_out, s));
+    FC_TRY(launch_sel_head(scores, nullptr, nullptr, 0, 0.f, 1, nullptr, nullptr, nullptr,
+                           static_cast<uint32_t*>(workspace), H, L, Bp, idx_out, static_cast<hipStream_t>(stream)));
     return FC_OK;
 }
 

@@ -33,6 +33,14 @@ template <> struct Frag8<kBF16> {
     uint4 u;  // 8 x bf16
     __device__ __forceinline__ void load(const void* p) { u = *reinterpret_cast<const uint4*>(p); }
     __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void unpack(float (&x)[8]) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
 };
 template <> struct Frag8<kF32> {
     float4 lo, hi;
@@ -41,6 +49,10 @@ template <> struct Frag8<kF32> {
         hi = reinterpret_cast<const float4*>(p)[1];
     }
     __device__ __forceinline__ void zero() { lo = hi = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void unpack(float (&x)[8]) const {
+        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+        x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+    }
 };
 
 // acc(32x32) += A(32 rows x 16 depth) * B(16 depth x 32 cols).

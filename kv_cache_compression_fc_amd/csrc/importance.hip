@@ -371,12 +371,30 @@ __device__ __forceinline__ float merged_lse2(const float2* __restrict__ ph, int 
 constexpr int kSmallThreads = 256;
 
 // Per query: the natural-log lse (optional) and -lse2 padded with -inf to
-// lq_pad (optional), from the pass-1 partials.
+// lq_pad (optional), from the pass-1 partials.  Block 0 of each head also
+// sums the redundancy partials u_part[h][0..nbu) into u[h] (fixed order).
 __global__ __launch_bounds__(kSmallThreads) void imp_lse_merge_kernel(const float2* __restrict__ part,
                                                                       float* __restrict__ lse,
                                                                       float* __restrict__ nlse2, int Lq, int lq_pad,
-                                                                      int nsplit) {
+                                                                      int nsplit, const float* __restrict__ u_part,
+                                                                      int nbu, float* __restrict__ u, int d) {
     const int h = blockIdx.y;
+    if (u_part != nullptr && blockIdx.x == 0) {
+        for (int c = threadIdx.x; c < d; c += kSmallThreads) {
+            // four independent chains keep four loads in flight
+            const float* pc = u_part + (size_t)h * nbu * d + c;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            int i = 0;
+            for (; i + 4 <= nbu; i += 4) {
+                a0 += pc[(size_t)i * d];
+                a1 += pc[(size_t)(i + 1) * d];
+                a2 += pc[(size_t)(i + 2) * d];
+                a3 += pc[(size_t)(i + 3) * d];
+            }
+            for (; i < nbu; ++i) a0 += pc[(size_t)i * d];
+            u[(size_t)h * d + c] = (a0 + a1) + (a2 + a3);
+        }
+    }
     const int q = blockIdx.x * kSmallThreads + threadIdx.x;
     if (q >= lq_pad) return;
     const float l2 = q < Lq ? merged_lse2(part + (size_t)h * nsplit * Lq, Lq, nsplit, q) : INFINITY;
@@ -392,13 +410,64 @@ __global__ __launch_bounds__(kSmallThreads) void imp_nlse2_kernel(const float* _
     if (q < lq_pad) nlse2[(size_t)h * lq_pad + q] = q < Lq ? -lse[(size_t)h * Lq + q] * kLog2e : -INFINITY;
 }
 
+// Redundancy of the keys a pass-2 workgroup holds in registers (Key designs
+// item 3: cosine similarity of l2-normalised keys, diagonal zeroed, averaged
+// over the L_k tokens).  With khat = k / max(||k||, 1e-12) and u = sum_i khat_i,
+//     r_j = (u . khat_j - khat_j . khat_j) / L_k.
+// Lane l holds depths 16*kk + 8*(l/32) .. +8 of key l%32, so the two halves
+// of the wave add their partial dot products.  Also writes the workgroup's
+// softmax partial (max, sum 2^(x - max)) of x = r * log2(e).
+template <int DT, int D>
+__device__ __forceinline__ void redundancy_of_keys(const Frag8<DT> (&kf)[D / 16], const float* __restrict__ uh,
+                                                   int key, int lane, int Lk, float* __restrict__ r_h,
+                                                   float2* __restrict__ red_out) {
+    __shared__ float2 wstat[kWaves];
+    const int half = lane >> 5;
+    float dot = 0.f, n2 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        float x[8];
+        kf[kk].unpack(x);
+        const float4 u0 = *reinterpret_cast<const float4*>(uh + 16 * kk + 8 * half);
+        const float4 u1 = *reinterpret_cast<const float4*>(uh + 16 * kk + 8 * half + 4);
+        const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dot = fmaf(x[e], uv[e], dot);
+            n2 = fmaf(x[e], x[e], n2);
+        }
+    }
+    dot += __shfl_xor(dot, 32, kWave);
+    n2 += __shfl_xor(n2, 32, kWave);
+    const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
+    const float rj = (dot * inv - n2 * inv * inv) / (float)Lk;
+    const bool own = lane < 32 && key < Lk;
+    if (own) r_h[key] = rj;
+    float m = own ? rj * kLog2e : -1e30f, s = own ? 1.f : 0.f;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+        lse2_merge(m, s, m2, s2);
+    }
+    if (lane == 0) wstat[threadIdx.x / kWave] = make_float2(m, s);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = wstat[0].x, S = wstat[0].y;
+        for (int w = 1; w < kWaves; ++w) lse2_merge(M, S, wstat[w].x, wstat[w].y);
+        *red_out = make_float2(M, S);
+    }
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum_kernel(const void* __restrict__ Q,
                                                                                const void* __restrict__ K,
                                                                                const float* __restrict__ nlse2,
                                                                                float* __restrict__ imp, int Lq,
                                                                                int lq_pad, int Lk, int nkb,
-                                                                               int n_items, float c, float inv_lq) {
+                                                                               int n_items, float c, float inv_lq,
+                                                                               const float* __restrict__ u,
+                                                                               float* __restrict__ r_out,
+                                                                               float2* __restrict__ red_part) {
     constexpr int kE = Elem<DT>::kBytes;
     constexpr int QT = tile_rows<DT>();
     constexpr int NKK = D / 16;
@@ -460,6 +529,8 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         if (key < Lk) kf[kk].load(Kh + ((size_t)key * D + 16 * kk + 8 * half) * kE);
         else kf[kk].zero();
     }
+    if (u != nullptr) redundancy_of_keys<DT, D>(kf, u + (size_t)h * D, key, lane, Lk, r_out + (size_t)h * Lk,
+                                                 red_part + (size_t)h * nkb + kblk);
     wait_vmcnt<L>();  // tile 0 landed (tile 1 may be in flight)
     tile_barrier();
 
@@ -539,12 +610,12 @@ hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq,
 
 template <int DT, int D>
 hipError_t colsum_launch(const void* Q, const void* K, const float* nlse2, float* imp, int H, int Lq, int Lk, float c,
-                         hipStream_t s) {
+                         hipStream_t s, const float* u, float* r, float2* red_part) {
     const int nkb = (Lk + kRowsPerBlock - 1) / kRowsPerBlock;
     const long long n_items = (long long)H * nkb;
     const int blocks = (int)((n_items + 7) / 8 * 8);
     hipLaunchKernelGGL((imp_colsum_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, nlse2, imp, Lq,
-                       imp_lq_pad(Lq), Lk, nkb, (int)n_items, c, 1.0f / (float)Lq);
+                       imp_lq_pad(Lq), Lk, nkb, (int)n_items, c, 1.0f / (float)Lq, u, r, red_part);
     return hipGetLastError();
 }
 
@@ -573,19 +644,21 @@ hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* p
                     : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s);
 }
 
+int imp_colsum_blocks(int Lk) { return (Lk + kRowsPerBlock - 1) / kRowsPerBlock; }
+
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
-                             int Lq, int Lk, float c, hipStream_t s) {
-    if (dt == kBF16) return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s)
-                                     : colsum_launch<kBF16, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s);
-    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s)
-                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s);
+                             int Lq, int Lk, float c, hipStream_t s, const float* u, float* r, float2* red_part) {
+    if (dt == kBF16) return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part)
+                                     : colsum_launch<kBF16, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part);
+    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part)
+                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part);
 }
 
 hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,
-                                hipStream_t s) {
+                                hipStream_t s, const float* u_part, int nbu, float* u, int d) {
     const int lq_pad = imp_lq_pad(Lq);
     hipLaunchKernelGGL(imp_lse_merge_kernel, dim3((lq_pad + kSmallThreads - 1) / kSmallThreads, H),
-                       dim3(kSmallThreads), 0, s, part, lse, nlse2, Lq, lq_pad, nsplit);
+                       dim3(kSmallThreads), 0, s, part, lse, nlse2, Lq, lq_pad, nsplit, u_part, nbu, u, d);
     return hipGetLastError();
 }
 

@@ -21,13 +21,20 @@ hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* p
 // Queries padded to whole pass-2 tiles.
 int imp_lq_pad(int Lq);
 // Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled
-// logits, negated, padded with -inf).
+// logits, negated, padded with -inf).  With u != nullptr ([H][d], the sum of
+// the normalised keys) pass 2 also writes the redundancy r [H][Lk] of the
+// keys it holds and one softmax partial (max, sum e^{r-max}, base 2) per
+// workgroup into red_part [H][imp_colsum_blocks(Lk)].
+int imp_colsum_blocks(int Lk);
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
-                             int Lq, int Lk, float c, hipStream_t s);
+                             int Lq, int Lk, float c, hipStream_t s, const float* u = nullptr,
+                             float* r = nullptr, float2* red_part = nullptr);
 // From the pass-1 partials: the natural-log lse [H][Lq] and/or -lse2 (either
-// may be nullptr).
+// may be nullptr).  With u_part != nullptr it also sums the redundancy
+// partials u_part [H][nbu][d] into u [H][d].
 hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,
-                                hipStream_t s);
+                                hipStream_t s, const float* u_part = nullptr, int nbu = 0, float* u = nullptr,
+                                int d = 0);
 // -lse2 from a natural-log lse.
 hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipStream_t s);
 
@@ -36,36 +43,21 @@ hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipSt
 int red_nbu(int Lk);
 int red_nbr(int Lk);
 // Pass A: per-block partial u = sum khat over the block's keys -> u_part[H][nbu][d].
-// Also zeroes hist0 (H * hist_words uint32) when hist != nullptr.
-hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk,
-                               uint32_t* hist, size_t hist_words, hipStream_t s);
+hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, hipStream_t s);
 // Pass B: r = (u.khat - khat.khat)/Lk and per-block softmax partials (max, sum e^{r-max}).
 hipError_t launch_red_dot(int dt, int d, const void* K, const float* u_part, float* r,
                           float2* red_part, int H, int Lk, hipStream_t s);
 // Softmax partials of a given r (used when r comes from the caller).
-hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, uint32_t* hist,
-                            size_t hist_words, hipStream_t s);
+hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, hipStream_t s);
 
 // ---- selection ----------------------------------------------------------------
-constexpr int kSelTile = 2048;  // keys per selection block
-constexpr int kHistBins = 4096;
-constexpr int kHistWordsPerHead = 3 * kHistBins;
-int sel_nblk(int L);
-struct SelBuffers {
-    uint32_t* keys;    // [H][L]
-    uint32_t* hist;    // [H][3][4096]
-    uint32_t* counts;  // [H][nblk][2]
-    uint32_t* state;   // [H][2]: threshold key, tie quota
-};
-// Keys (and histogram round 0) from importance + redundancy, or from scores.
-hipError_t launch_sel_keys_from_imp(const float* imp, const float* r, const float2* red_part, int nbr,
-                                    float lam, int w, float* score_out, float* imp_pooled_out,
-                                    float* red_out, const SelBuffers& b, int H, int L, hipStream_t s);
-hipError_t launch_sel_keys_from_scores(const float* scores, const SelBuffers& b, int H, int L,
-                                       hipStream_t s);
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
-// Radix refinement, counting and compaction into idx_out [H][Bp].
-hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int32_t* idx_out, hipStream_t s);
+// One workgroup per head: scores (from importance + redundancy when r != nullptr,
+// else `src` holds them), order-preserving keys (spilled to keys [H][L] when a
+// head exceeds one chunk), radix select of the B' largest and the ordered
+// compaction into idx_out [H][Bp].
+hipError_t launch_sel_head(const float* src, const float* r, const float2* red_part, int nbr, float lam, int w,
+                           float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H, int L,
+                           int Bp, int32_t* idx_out, hipStream_t s);
 // K_out[h][b] = K[h][idx[h][b]], V likewise.
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
                          void* K_out, void* V_out, hipStream_t s);

@@ -45,24 +45,13 @@ __device__ __forceinline__ void load_vec<kF32>(const void* p, float* x) {
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
 
-__device__ __forceinline__ void zero_slice(uint32_t* hist, size_t words, int blk, int nblk) {
-    if (hist == nullptr) return;
-    const size_t per = (words + nblk - 1) / nblk;
-    const size_t b = (size_t)blk * per;
-    const size_t e = b + per < words ? b + per : words;
-    for (size_t i = b + threadIdx.x; i < e; i += kThreads) hist[i] = 0u;
-}
-
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void red_norm_sum_kernel(const void* __restrict__ K,
-                                                                float* __restrict__ u_part, int Lk,
-                                                                uint32_t* __restrict__ hist,
-                                                                size_t hist_words) {
+                                                                float* __restrict__ u_part, int Lk) {
     using RL = RowLayout<DT, D>;
     constexpr int kE = Elem<DT>::kBytes;
     __shared__ float red[RL::kRpi][D];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    zero_slice(hist ? hist + (size_t)h * hist_words : nullptr, hist_words, blk, nblk);
 
     const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
     const int rows = (Lk + nblk - 1) / nblk;
@@ -183,11 +172,8 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
 }
 
 __global__ __launch_bounds__(kThreads) void red_stats_kernel(const float* __restrict__ r,
-                                                             float2* __restrict__ red_part, int Lk,
-                                                             uint32_t* __restrict__ hist,
-                                                             size_t hist_words) {
+                                                             float2* __restrict__ red_part, int Lk) {
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    zero_slice(hist ? hist + (size_t)h * hist_words : nullptr, hist_words, blk, nblk);
     const int rows = (Lk + nblk - 1) / nblk;
     const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
     float m = -1e30f, s = 0.f;
@@ -196,10 +182,8 @@ __global__ __launch_bounds__(kThreads) void red_stats_kernel(const float* __rest
 }
 
 template <int DT, int D>
-hipError_t norm_sum_launch(const void* K, float* u_part, int H, int Lk, uint32_t* hist, size_t hist_words,
-                           hipStream_t s) {
-    hipLaunchKernelGGL((red_norm_sum_kernel<DT, D>), dim3(red_nbu(Lk), H), dim3(kThreads), 0, s, K, u_part,
-                       Lk, hist, hist_words);
+hipError_t norm_sum_launch(const void* K, float* u_part, int H, int Lk, hipStream_t s) {
+    hipLaunchKernelGGL((red_norm_sum_kernel<DT, D>), dim3(red_nbu(Lk), H), dim3(kThreads), 0, s, K, u_part, Lk);
     return hipGetLastError();
 }
 template <int DT, int D>
@@ -221,12 +205,11 @@ int red_nbr(int Lk) {
     return n < 1 ? 1 : (n > 128 ? 128 : n);
 }
 
-hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, uint32_t* hist,
-                               size_t hist_words, hipStream_t s) {
-    if (dt == kBF16) return d == 128 ? norm_sum_launch<kBF16, 128>(K, u_part, H, Lk, hist, hist_words, s)
-                                     : norm_sum_launch<kBF16, 64>(K, u_part, H, Lk, hist, hist_words, s);
-    return d == 128 ? norm_sum_launch<kF32, 128>(K, u_part, H, Lk, hist, hist_words, s)
-                    : norm_sum_launch<kF32, 64>(K, u_part, H, Lk, hist, hist_words, s);
+hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, hipStream_t s) {
+    if (dt == kBF16) return d == 128 ? norm_sum_launch<kBF16, 128>(K, u_part, H, Lk, s)
+                                     : norm_sum_launch<kBF16, 64>(K, u_part, H, Lk, s);
+    return d == 128 ? norm_sum_launch<kF32, 128>(K, u_part, H, Lk, s)
+                    : norm_sum_launch<kF32, 64>(K, u_part, H, Lk, s);
 }
 
 hipError_t launch_red_dot(int dt, int d, const void* K, const float* u_part, float* r, float2* red_part,
@@ -237,10 +220,8 @@ hipError_t launch_red_dot(int dt, int d, const void* K, const float* u_part, flo
                     : dot_launch<kF32, 64>(K, u_part, r, red_part, H, Lk, s);
 }
 
-hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, uint32_t* hist, size_t hist_words,
-                            hipStream_t s) {
-    hipLaunchKernelGGL(red_stats_kernel, dim3(red_nbr(Lk), H), dim3(kThreads), 0, s, r, red_part, Lk, hist,
-                       hist_words);
+hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, hipStream_t s) {
+    hipLaunchKernelGGL(red_stats_kernel, dim3(red_nbr(Lk), H), dim3(kThreads), 0, s, r, red_part, Lk);
     return hipGetLastError();
 }
 

@@ -6,14 +6,23 @@
 // and each head keeps its B' = min(B, L) best tokens (flowchart under
 // 整体框架: cache full -> joint score -> top-B per head).
 //
-// Selection is exact on the float32 scores: each score becomes an
-// order-preserving uint32 key, a three-round radix select (12 + 12 + 8 bits,
-// LDS histograms merged with integer atomics) finds the B'-th largest key T
-// and the number q of keys equal to T that fit, and a compaction keeps every
-// key > T plus the first q keys == T in token order (ties go to the lower
-// index).  Kept tokens are written in ascending token order, and a gather
-// kernel with one block per 64 kept rows copies their K and V rows.  Integer
-// atomics only, so the result is deterministic.
+// One 1024-thread workgroup per head does the whole selection, exactly, on
+// the float32 scores.  Each score becomes an order-preserving uint32 key;
+// three radix rounds (8 + 12 + 12 bits) with LDS histograms find the B'-th
+// largest key T and the number q of keys equal to T that fit.  The scores of
+// one head sit in a narrow range, so the top key bits (sign and exponent) put
+// most keys into a few bins: every bin is kept in several copies, picked by
+// the lane, which bounds the lanes of one atomic instruction that meet at one
+// address.  An ordered compaction keeps every key > T plus the first q keys
+// == T in token order (ties go to the lower index) and writes the kept
+// indices ascending.  Keys are processed in chunks of 18 consecutive keys per
+// thread, staged through LDS so that every global access is coalesced; a head
+// that fits one chunk keeps its keys in LDS between the passes, a longer one
+// re-reads them from the workspace.  No global atomics: the result is
+// deterministic.  A gather kernel with one block per 64 kept rows then copies
+// their K and V rows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,9 +30,13 @@ namespace fc {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPer = kSelTile / kThreads;  // consecutive keys per thread
-static_assert(kPer * kThreads == kSelTile, "tile");
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kKpt = 18;                      // consecutive keys per thread per chunk
+constexpr int kChunk = kSelThreads * kKpt;    // 18432 keys per chunk
+constexpr int kMaxHalo = 64;                  // pool half-window limit ((w-1)/2 <= 64)
+constexpr int kRegHalo = 4;                   // half-windows served from registers
+constexpr int kAWords = kMaxHalo + kChunk + kMaxHalo;  // LDS area A: importance tile / histograms / staging
 
 // Larger float -> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -31,284 +44,307 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-level search of a histogram for the bin holding the k-th largest
-// element (k >= 1).  Returns the bin; *k_in_bin receives k minus the count in
-// higher bins.  All threads get the result.
-template <int BINS>
-__device__ __forceinline__ int find_bin_from_top(const uint32_t* __restrict__ hist, uint32_t k,
-                                                 uint32_t* k_in_bin) {
-    constexpr int kPerT = BINS / kThreads;
-    __shared__ uint32_t scan_lds[4];
-    __shared__ int found_bin;
-    __shared__ uint32_t found_k;
-    // thread t owns bins BINS-1-(t*kPerT + i), i.e. descending order
+// Exclusive prefix sum over the workgroup; *total receives the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += t;
+    }
+    if (lane == kWave - 1) lds[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const uint32_t x = lds[w];
+        before += w < wave ? x : 0u;
+        tot += x;
+    }
+    *total = tot;
+    __syncthreads();
+    return before + inc - v;
+}
+
+// The bin of an LDS histogram of BINS bins, each kept in COPIES copies
+// (word bin*COPIES + copy), that holds the k-th largest element (k >= 1), and
+// k minus the count of the higher bins; every thread gets both.
+template <int BINS, int COPIES>
+__device__ __forceinline__ uint32_t find_bin_from_top(const uint32_t* hist, uint32_t k, uint32_t* k_in_bin,
+                                                      uint32_t* scan_lds, uint32_t* s_res) {
+    constexpr int kPerT = BINS >= kSelThreads ? BINS / kSelThreads : 1;
+    constexpr int kActive = BINS / kPerT;
+    // thread t owns bins BINS-1-(t*kPerT + i): descending order
     uint32_t cnt[kPerT];
     uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < kPerT; ++i) {
-        cnt[i] = hist[BINS - 1 - (threadIdx.x * kPerT + i)];
-        sum += cnt[i];
+        uint32_t c = 0;
+        if (threadIdx.x < kActive) {
+            const uint32_t* hb = hist + (BINS - 1 - (threadIdx.x * kPerT + i)) * COPIES;
+#pragma unroll
+            for (int cp = 0; cp < COPIES; ++cp) c += hb[cp];
+        }
+        cnt[i] = c;
+        sum += c;
     }
     uint32_t total;
-    const uint32_t before = block256_exclusive_scan(sum, scan_lds, &total);
-    if (before < k && k <= before + sum) {
+    const uint32_t before = block_exclusive_scan(sum, scan_lds, &total);
+    if (sum > 0 && before < k && k <= before + sum) {
         uint32_t acc = before;
         for (int i = 0; i < kPerT; ++i) {
             if (acc + cnt[i] >= k) {
-                found_bin = BINS - 1 - (threadIdx.x * kPerT + i);
-                found_k = k - acc;
+                s_res[0] = BINS - 1 - (threadIdx.x * kPerT + i);
+                s_res[1] = k - acc;
                 break;
             }
             acc += cnt[i];
         }
     }
     __syncthreads();
-    *k_in_bin = found_k;
-    const int b = found_bin;
+    *k_in_bin = s_res[1];
+    const uint32_t b = s_res[0];
     __syncthreads();
     return b;
 }
 
-// Prefix (bits above the current round) and remaining rank after `rounds`
-// completed rounds.
-struct RadixState {
-    uint32_t prefix;  // key bits fixed so far (in place)
-    uint32_t k;       // rank still to find within the keys matching prefix
-};
-__device__ __forceinline__ RadixState radix_state(const uint32_t* __restrict__ hist_h, uint32_t Bp, int rounds) {
-    RadixState st{0u, Bp};
-    if (rounds >= 1) {
-        uint32_t k1;
-        const int b0 = find_bin_from_top<kHistBins>(hist_h, st.k, &k1);
-        st.prefix = (uint32_t)b0 << 20;
-        st.k = k1;
-    }
-    if (rounds >= 2) {
-        uint32_t k2;
-        const int b1 = find_bin_from_top<kHistBins>(hist_h + kHistBins, st.k, &k2);
-        st.prefix |= (uint32_t)b1 << 8;
-        st.k = k2;
-    }
-    if (rounds >= 3) {
-        uint32_t k3;
-        const int b2 = find_bin_from_top<256>(hist_h + 2 * kHistBins, st.k, &k3);
-        st.prefix |= (uint32_t)b2;
-        st.k = k3;
-    }
-    return st;
-}
-
-// Adds a block's LDS histogram into the global one (non-zero bins only).
-template <int BINS>
-__device__ __forceinline__ void flush_hist(const uint32_t* lh, uint32_t* gh) {
-    for (int b = threadIdx.x; b < BINS; b += kThreads) {
-        const uint32_t c = lh[b];
-        if (c) atomicAdd(gh + b, c);
-    }
-}
-
-__device__ __forceinline__ void zero_rounds_1_2(uint32_t* hist_h, int blk, int nblk) {
-    // rounds 1 and 2 of this head's histogram, split over the head's blocks
-    const int words = 2 * kHistBins;
-    const int per = (words + nblk - 1) / nblk;
-    const int b = blk * per, e = min(words, b + per);
-    for (int i = b + threadIdx.x; i < e; i += kThreads) hist_h[kHistBins + i] = 0u;
-}
-
-// Round 0: keys from pooled importance and redundancy softmax.
-__global__ __launch_bounds__(kThreads) void sel_keys_from_imp_kernel(
-    const float* __restrict__ imp, const float* __restrict__ r, const float2* __restrict__ red_part, int nbr,
+// kFromImp: scores from importance (pooled here) and redundancy r with its
+// softmax partials red_part [H][nbr]; otherwise `src` holds the scores.
+template <bool kFromImp>
+__global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
+    const float* __restrict__ src, const float* __restrict__ r, const float2* __restrict__ red_part, int nbr,
     float lam, int hw, float* __restrict__ score_out, float* __restrict__ imp_pooled_out,
-    float* __restrict__ red_out, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist, int L) {
-    __shared__ float tile[kSelTile + 2 * 64];
-    __shared__ uint32_t lh[kHistBins];
+    float* __restrict__ red_out, uint32_t* __restrict__ keys, int L, int Bp, int32_t* __restrict__ idx_out) {
+    // Area A: the chunk's importance with its halo (tile_a[kMaxHalo + x] =
+    // Imp[c0 + x]) while the keys are formed, then the radix histograms, then
+    // the staging of the kept indices.  tile_b: the chunk's r (or scores),
+    // then its keys.
+    __shared__ __align__(16) uint32_t area_a[kAWords];
+    __shared__ __align__(16) uint32_t tile_b[kChunk];
+    __shared__ uint32_t scan_lds[kSelWaves];
+    float* const tile_a = reinterpret_cast<float*>(area_a);
+    uint32_t* const hist = area_a;
+    __shared__ uint32_t s_res[2];
     __shared__ float stat[2];
-    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    const int j0 = blk * kSelTile;
-    const float* imph = imp + (size_t)h * L;
-    for (int b = threadIdx.x; b < kHistBins; b += kThreads) lh[b] = 0u;
-    zero_rounds_1_2(hist + (size_t)h * kHistWordsPerHead, blk, nblk);
-    // importance tile with a halo of hw on each side (hw <= 64)
-    for (int i = threadIdx.x; i < kSelTile + 2 * hw; i += kThreads) {
-        const int j = j0 - hw + i;
-        tile[i] = (j >= 0 && j < L) ? imph[j] : -INFINITY;
-    }
-    if (threadIdx.x == 0) {
-        float M = -1e30f, S = 0.f;
-        for (int i = 0; i < nbr; ++i) {
-            const float2 v = red_part[(size_t)h * nbr + i];
-            lse2_merge(M, S, v.x, v.y);
-        }
-        stat[0] = M;            // max of r * log2e
-        stat[1] = 1.0f / S;     // 1 / sum 2^{r*log2e - M}
-    }
-    __syncthreads();
-    const float M = stat[0], invS = stat[1];
-    const float lam_red = 1.0f - lam;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int lj = threadIdx.x * kPer + i;
-        const int j = j0 + lj;
-        if (j >= L) break;
-        float pooled = tile[lj + hw];
-        for (int o = 1; o <= hw; ++o) pooled = fmaxf(pooled, fmaxf(tile[lj + hw - o], tile[lj + hw + o]));
-        const float red = exp2_hw(fmaf(r[(size_t)h * L + j], kLog2e, -M)) * invS;
-        const float sc = lam * pooled - lam_red * red;
-        const size_t o = (size_t)h * L + j;
-        if (score_out) score_out[o] = sc;
-        if (imp_pooled_out) imp_pooled_out[o] = pooled;
-        if (red_out) red_out[o] = red;
-        const uint32_t key = order_key(sc);
-        keys[o] = key;
-        atomicAdd(&lh[key >> 20], 1u);
-    }
-    __syncthreads();
-    flush_hist<kHistBins>(lh, hist + (size_t)h * kHistWordsPerHead);
-}
 
-// Round 0 from given scores.
-__global__ __launch_bounds__(kThreads) void sel_keys_from_scores_kernel(const float* __restrict__ scores,
-                                                                        uint32_t* __restrict__ keys,
-                                                                        uint32_t* __restrict__ hist, int L) {
-    __shared__ uint32_t lh[kHistBins];
-    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    for (int b = threadIdx.x; b < kHistBins; b += kThreads) lh[b] = 0u;
-    zero_rounds_1_2(hist + (size_t)h * kHistWordsPerHead, blk, nblk);
-    __syncthreads();
-    const int j0 = blk * kSelTile;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + threadIdx.x + kThreads * i;
-        if (j < L) {
-            const uint32_t key = order_key(scores[(size_t)h * L + j]);
-            keys[(size_t)h * L + j] = key;
-            atomicAdd(&lh[key >> 20], 1u);
-        }
-    }
-    __syncthreads();
-    flush_hist<kHistBins>(lh, hist + (size_t)h * kHistWordsPerHead);
-}
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const size_t hL = (size_t)h * L;
+    const int nch = (L + kChunk - 1) / kChunk;
+    const bool cached = nch == 1;  // the keys stay in tile_b between the passes
+    const int x0 = tid * kKpt;     // this thread's first key in a chunk
 
-// Rounds 1 (bits 19..8) and 2 (bits 7..0) over the keys matching the prefix.
-template <int ROUND>
-__global__ __launch_bounds__(kThreads) void sel_refine_kernel(const uint32_t* __restrict__ keys,
-                                                              uint32_t* __restrict__ hist, int L, int Bp) {
-    constexpr int BINS = ROUND == 1 ? kHistBins : 256;
-    __shared__ uint32_t lh[BINS];
-    const int h = blockIdx.y, blk = blockIdx.x;
-    uint32_t* hist_h = hist + (size_t)h * kHistWordsPerHead;
-    for (int b = threadIdx.x; b < BINS; b += kThreads) lh[b] = 0u;
-    const RadixState st = radix_state(hist_h, (uint32_t)Bp, ROUND);
-    const uint32_t shift = ROUND == 1 ? 20u : 8u;
-    const uint32_t want = st.prefix >> shift;
-    const int j0 = blk * kSelTile;
+    // softmax statistics of r: (max of r*log2e, 1 / sum 2^{r*log2e - max})
+    if constexpr (kFromImp) {
+        if (tid < kWave) {
+            float M = -1e30f, S = 0.f;
+            for (int i = tid; i < nbr; i += kWave) {
+                const float2 v = red_part[(size_t)h * nbr + i];
+                lse2_merge(M, S, v.x, v.y);
+            }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + threadIdx.x + kThreads * i;
-        if (j < L) {
-            const uint32_t key = keys[(size_t)h * L + j];
-            if ((key >> shift) == want) {
-                const uint32_t dig = ROUND == 1 ? ((key >> 8) & 0xfffu) : (key & 0xffu);
-                atomicAdd(&lh[dig], 1u);
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+                lse2_merge(M, S, m2, s2);
+            }
+            if (tid == 0) {
+                stat[0] = M;
+                stat[1] = 1.0f / S;
             }
         }
     }
-    __syncthreads();
-    flush_hist<BINS>(lh, hist_h + ROUND * kHistBins);
-}
 
-// Threshold T (the B'-th largest key), quota q of keys == T, and per-block counts.
-__global__ __launch_bounds__(kThreads) void sel_count_kernel(const uint32_t* __restrict__ keys,
-                                                             const uint32_t* __restrict__ hist,
-                                                             uint32_t* __restrict__ counts,
-                                                             uint32_t* __restrict__ state, int L, int Bp) {
-    __shared__ uint32_t scan_lds[4];
-    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    const RadixState st = radix_state(hist + (size_t)h * kHistWordsPerHead, (uint32_t)Bp, 3);
-    const uint32_t T = st.prefix;
-    const int j0 = blk * kSelTile;
-    uint32_t gt = 0, eq = 0;
+    // ---- keys --------------------------------------------------------------------------
+    for (int c = 0; c < nch; ++c) {
+        const int c0 = c * kChunk;
+        const int n = min(kChunk, L - c0);
+        // all loads of the chunk in flight at once, then the LDS stores
+        {
+            const float* rs = (kFromImp ? r : src) + hL + c0;
+            float v[kKpt];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + threadIdx.x + kThreads * i;
-        if (j < L) {
-            const uint32_t key = keys[(size_t)h * L + j];
-            gt += key > T;
-            eq += key == T;
+            for (int q = 0; q < kKpt; ++q) {
+                const int i = tid + q * kSelThreads;
+                v[q] = i < n ? rs[i] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = __float_as_uint(v[q]);
+        }
+        if constexpr (kFromImp) {
+            // importance with a halo of hw <= kMaxHalo on each side
+            constexpr int kQa = (kChunk + 2 * kMaxHalo + kSelThreads - 1) / kSelThreads;
+            float v[kQa];
+#pragma unroll
+            for (int q = 0; q < kQa; ++q) {
+                const int i = tid + q * kSelThreads, j = c0 - hw + i;
+                v[q] = (i < kChunk + 2 * hw && j >= 0 && j < L) ? src[hL + j] : -INFINITY;
+            }
+#pragma unroll
+            for (int q = 0; q < kQa; ++q) {
+                const int i = tid + q * kSelThreads;
+                if (i < kChunk + 2 * hw) tile_a[kMaxHalo - hw + i] = v[q];
+            }
+        }
+        __syncthreads();
+        const float M = kFromImp ? stat[0] : 0.f, invS = kFromImp ? stat[1] : 0.f;
+        float pooled[kKpt];
+        if constexpr (kFromImp) {
+            if (hw <= kRegHalo) {
+                float v[kKpt + 2 * kRegHalo];
+                const float2* t2 = reinterpret_cast<const float2*>(tile_a + kMaxHalo - kRegHalo + x0);
+#pragma unroll
+                for (int q = 0; q < (kKpt + 2 * kRegHalo) / 2; ++q) {
+                    const float2 f = t2[q];
+                    v[2 * q] = f.x;
+                    v[2 * q + 1] = f.y;
+                }
+#pragma unroll
+                for (int i = 0; i < kKpt; ++i) {
+                    float p = v[kRegHalo + i];
+#pragma unroll
+                    for (int o = 1; o <= kRegHalo; ++o)
+                        if (o <= hw) p = fmaxf(p, fmaxf(v[kRegHalo + i - o], v[kRegHalo + i + o]));
+                    pooled[i] = p;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kKpt; ++i) {
+                    const float* t = tile_a + kMaxHalo + x0 + i;
+                    float p = t[0];
+                    for (int o = 1; o <= hw; ++o) p = fmaxf(p, fmaxf(t[-o], t[o]));
+                    pooled[i] = p;
+                }
+            }
+        }
+        uint2* tb2 = reinterpret_cast<uint2*>(tile_b + x0);
+#pragma unroll
+        for (int q = 0; q < kKpt / 2; ++q) {
+            const uint2 in = tb2[q];
+            uint32_t out[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * q + e;
+                const int j = c0 + x0 + i;
+                const float x = __uint_as_float(e == 0 ? in.x : in.y);
+                float sc = x;
+                if constexpr (kFromImp) {
+                    const float red = exp2_hw(fmaf(x, kLog2e, -M)) * invS;
+                    sc = lam * pooled[i] - (1.0f - lam) * red;
+                    if (j < L) {
+                        if (score_out) score_out[hL + j] = sc;
+                        if (imp_pooled_out) imp_pooled_out[hL + j] = pooled[i];
+                        if (red_out) red_out[hL + j] = red;
+                    }
+                }
+                out[e] = order_key(sc);
+            }
+            tb2[q] = make_uint2(out[0], out[1]);  // this thread's own slots
+        }
+        if (!cached) {
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kKpt; ++q) {
+                const int i = tid + q * kSelThreads;
+                if (i < n) keys[hL + c0 + i] = tile_b[i];
+            }
+            __syncthreads();  // the tiles are refilled by the next chunk
         }
     }
-    uint32_t tgt, teq;
-    block256_exclusive_scan(gt, scan_lds, &tgt);
-    block256_exclusive_scan(eq, scan_lds, &teq);
-    if (threadIdx.x == 0) {
-        counts[((size_t)h * nblk + blk) * 2 + 0] = tgt;
-        counts[((size_t)h * nblk + blk) * 2 + 1] = teq;
-        if (blk == 0) {
-            state[2 * h + 0] = T;
-            state[2 * h + 1] = st.k;
+    __syncthreads();  // area A (the importance tile) becomes the histograms
+    // this thread's keys of chunk c (from tile_b; staged there when not cached)
+    auto load_keys = [&](int c, uint32_t (&kv)[kKpt]) {
+        if (!cached) {
+            const int c0 = c * kChunk, n = min(kChunk, L - c0);
+            uint32_t v[kKpt];
+#pragma unroll
+            for (int q = 0; q < kKpt; ++q) {
+                const int i = tid + q * kSelThreads;
+                v[q] = i < n ? keys[hL + c0 + i] : 0u;
+            }
+            __syncthreads();  // everybody is done with the previous contents
+#pragma unroll
+            for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = v[q];
+            __syncthreads();
         }
-    }
-}
+        const uint2* tb2 = reinterpret_cast<const uint2*>(tile_b + x0);
+#pragma unroll
+        for (int q = 0; q < kKpt / 2; ++q) {
+            const uint2 v = tb2[q];
+            kv[2 * q] = v.x;
+            kv[2 * q + 1] = v.y;
+        }
+    };
 
-// Compaction in token order: every kept token's index at its output slot.
-__global__ __launch_bounds__(kThreads) void sel_compact_kernel(const uint32_t* __restrict__ keys,
-                                                               const uint32_t* __restrict__ counts,
-                                                               const uint32_t* __restrict__ state, int L, int Bp,
-                                                               int32_t* __restrict__ idx_out) {
-    __shared__ uint32_t scan_lds[4];
-    __shared__ uint32_t base_lds[2];
-    const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    const uint32_t T = state[2 * h + 0], q = state[2 * h + 1];
-    if (threadIdx.x < kWave) {
-        uint32_t gb = 0, eb = 0;
-        for (int b = threadIdx.x; b < blk; b += kWave) {
-            gb += counts[((size_t)h * nblk + b) * 2 + 0];
-            eb += counts[((size_t)h * nblk + b) * 2 + 1];
+    // ---- radix rounds: bits 31..24, 23..12, 11..0 ---------------------------------
+    // (a round's histogram counts the keys that match the bits fixed so far)
+    const uint32_t copy16 = tid & 15u, copy4 = tid & 3u;
+    auto round = [&](auto bits_c, auto copies_c, int sh, uint32_t pre, int pre_sh, uint32_t copy) {
+        constexpr int kBitsR = decltype(bits_c)::value, kCopies = decltype(copies_c)::value;
+        for (int b = tid; b < (1 << kBitsR) * kCopies; b += kSelThreads) hist[b] = 0u;
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            uint32_t kv[kKpt];
+            load_keys(c, kv);
+            const int j0 = c * kChunk + x0;
+#pragma unroll
+            for (int i = 0; i < kKpt; ++i) {
+                const bool match = j0 + i < L && (pre_sh >= 32 || (kv[i] >> pre_sh) == pre);
+                if (match) atomicAdd(&hist[((kv[i] >> sh) & ((1u << kBitsR) - 1u)) * kCopies + copy], 1u);
+            }
         }
-        gb = wave_sum(gb);
-        eb = wave_sum(eb);
-        if (threadIdx.x == 0) { base_lds[0] = gb; base_lds[1] = eb; }
-    }
-    __syncthreads();
-    const uint32_t gt_before = base_lds[0], eq_before = base_lds[1];
-    const uint32_t out_base = gt_before + min(eq_before, q);
+        __syncthreads();
+    };
+    uint32_t k1, k2, q;
+    round(std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{}, 24, 0u, 32, copy16);
+    const uint32_t b0 = find_bin_from_top<256, 16>(hist, (uint32_t)Bp, &k1, scan_lds, s_res);
+    round(std::integral_constant<int, 12>{}, std::integral_constant<int, 4>{}, 12, b0, 24, copy4);
+    const uint32_t b1 = find_bin_from_top<4096, 4>(hist, k1, &k2, scan_lds, s_res);
+    const uint32_t pre2 = (b0 << 12) | b1;  // bits 31..12
+    round(std::integral_constant<int, 12>{}, std::integral_constant<int, 4>{}, 0, pre2, 12, copy4);
+    const uint32_t b2 = find_bin_from_top<4096, 4>(hist, k2, &q, scan_lds, s_res);
+    const uint32_t T = (pre2 << 12) | b2;  // the B'-th largest key; q of the keys equal to T fit
 
-    const int j0 = blk * kSelTile + threadIdx.x * kPer;  // this thread's consecutive keys
-    uint32_t kv[kPer];
-    uint32_t neq = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + i;
-        kv[i] = j < L ? keys[(size_t)h * L + j] : 0u;
-        neq += (j < L && kv[i] == T);
-    }
-    uint32_t teq;
-    uint32_t eq_rank = eq_before + block256_exclusive_scan(neq, scan_lds, &teq);
-    uint32_t sel_mask = 0, nsel = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = j0 + i;
-        bool s = false;
-        if (j < L) {
-            if (kv[i] > T) s = true;
-            else if (kv[i] == T) { s = eq_rank < q; ++eq_rank; }
-        }
-        if (s) { sel_mask |= 1u << i; ++nsel; }
-    }
-    uint32_t tsel;
-    uint32_t pos = out_base + block256_exclusive_scan(nsel, scan_lds, &tsel);
+    // ---- ordered compaction -------------------------------------------------------
     int32_t* idx_h = idx_out + (size_t)h * Bp;
+    uint32_t out_pos = 0, eq_seen = 0;
+    for (int c = 0; c < nch; ++c) {
+        uint32_t kv[kKpt];
+        load_keys(c, kv);
+        const int j0 = c * kChunk + x0;
+        uint32_t neq = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        if (sel_mask & (1u << i)) {
-            if (pos < (uint32_t)Bp) idx_h[pos] = j0 + i;  // always true when the counts agree
-            ++pos;
+        for (int i = 0; i < kKpt; ++i) neq += (j0 + i < L && kv[i] == T);
+        uint32_t tot_eq, tot_sel;
+        uint32_t eq_rank = eq_seen + block_exclusive_scan(neq, scan_lds, &tot_eq);
+        uint32_t sel = 0, nsel = 0;
+#pragma unroll
+        for (int i = 0; i < kKpt; ++i) {
+            bool s = false;
+            if (j0 + i < L) {
+                if (kv[i] > T) s = true;
+                else if (kv[i] == T) { s = eq_rank < q; ++eq_rank; }
+            }
+            if (s) { sel |= 1u << i; ++nsel; }
         }
+        // kept indices go to their slots of this chunk's output in area A,
+        // then out with coalesced stores
+        uint32_t pos = block_exclusive_scan(nsel, scan_lds, &tot_sel);
+#pragma unroll
+        for (int i = 0; i < kKpt; ++i) {
+            if (sel & (1u << i)) area_a[pos++] = (uint32_t)(j0 + i);
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < tot_sel; i += kSelThreads)
+            if (out_pos + i < (uint32_t)Bp) idx_h[out_pos + i] = (int32_t)area_a[i];  // always true when the counts agree
+        __syncthreads();
+        out_pos += tot_sel;
+        eq_seen += tot_eq;
     }
 }
 
 // K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
 // kRowBytes/16 lanes, kGatherRows output rows per block.
+constexpr int kThreads = 256;
 constexpr int kGatherRows = 64;
 
 template <int DT, int D>
@@ -350,11 +386,6 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __
     }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-}
-
 template <int DT, int D>
 hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
                          void* V_out, hipStream_t s) {
@@ -365,33 +396,15 @@ hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K
 
 }  // namespace
 
-int sel_nblk(int L) { return (L + kSelTile - 1) / kSelTile; }
-
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(kThreads), 0, s, p, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_sel_keys_from_imp(const float* imp, const float* r, const float2* red_part, int nbr, float lam,
-                                    int w, float* score_out, float* imp_pooled_out, float* red_out,
-                                    const SelBuffers& b, int H, int L, hipStream_t s) {
-    hipLaunchKernelGGL(sel_keys_from_imp_kernel, dim3(sel_nblk(L), H), dim3(kThreads), 0, s, imp, r, red_part,
-                       nbr, lam, (w - 1) / 2, score_out, imp_pooled_out, red_out, b.keys, b.hist, L);
-    return hipGetLastError();
-}
-
-hipError_t launch_sel_keys_from_scores(const float* scores, const SelBuffers& b, int H, int L, hipStream_t s) {
-    hipLaunchKernelGGL(sel_keys_from_scores_kernel, dim3(sel_nblk(L), H), dim3(kThreads), 0, s, scores, b.keys,
-                       b.hist, L);
-    return hipGetLastError();
-}
-
-hipError_t launch_sel_finish(const SelBuffers& b, int H, int L, int Bp, int32_t* idx_out, hipStream_t s) {
-    const dim3 grid(sel_nblk(L), H);
-    hipLaunchKernelGGL(sel_refine_kernel<1>, grid, dim3(kThreads), 0, s, b.keys, b.hist, L, Bp);
-    hipLaunchKernelGGL(sel_refine_kernel<2>, grid, dim3(kThreads), 0, s, b.keys, b.hist, L, Bp);
-    hipLaunchKernelGGL(sel_count_kernel, grid, dim3(kThreads), 0, s, b.keys, b.hist, b.counts, b.state, L, Bp);
-    hipLaunchKernelGGL(sel_compact_kernel, grid, dim3(kThreads), 0, s, b.keys, b.counts, b.state, L, Bp, idx_out);
+hipError_t launch_sel_head(const float* src, const float* r, const float2* red_part, int nbr, float lam, int w,
+                           float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H, int L,
+                           int Bp, int32_t* idx_out, hipStream_t s) {
+    if (r != nullptr)
+        hipLaunchKernelGGL(sel_head_kernel<true>, dim3(H), dim3(kSelThreads), 0, s, src, r, red_part, nbr, lam,
+                           (w - 1) / 2, score_out, imp_pooled_out, red_out, keys, L, Bp, idx_out);
+    else
+        hipLaunchKernelGGL(sel_head_kernel<false>, dim3(H), dim3(kSelThreads), 0, s, src, nullptr, nullptr, 0, 0.f,
+                           0, nullptr, nullptr, nullptr, keys, L, Bp, idx_out);
     return hipGetLastError();
 }
 
