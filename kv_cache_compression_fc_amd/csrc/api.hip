@@ -43,7 +43,7 @@ fc_status check_kv(const fc_kv_params* p) {
 KvLayout kv_layout(const fc_kv_params* p) {
     KvLayout L{};
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
-    L.plan = imp_plan(p->H, p->L_q, p->L_k, dt);
+    L.plan = imp_plan(p->H, p->L_q, p->L_k, dt, p->d);
     L.nbu = red_nbu(p->L_k);
     L.nbr = red_nbr(p->L_k);
     L.nkb = imp_colsum_blocks(p->L_k);
@@ -51,7 +51,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
     L.nlse2 = o;    o = align_up(o + H * (size_t)imp_lq_pad(p->L_q) * sizeof(float));
-    L.imp = o;      o = align_up(o + H * Lk * sizeof(float));
+    L.imp = o;      o = align_up(o + (size_t)L.plan.nqs * H * Lk * sizeof(float));  // importance planes
     L.r = o;        o = align_up(o + H * Lk * sizeof(float));
     L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
     L.u = o;        o = align_up(o + H * (size_t)p->d * sizeof(float));
@@ -77,21 +77,26 @@ fc_status hip_status(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_HIP
         if (e_ != hipSuccess) return FC_ERR_HIP;     \
     } while (0)
 
-// Importance (two passes).  With `r` the second pass also produces the
-// redundancy of the keys it holds (u from the partials red_norm_sum left in
-// the workspace) and the softmax partials of r, one per workgroup.
-fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp,
+// Importance (two passes) into the workspace's importance planes; with
+// imp_out they are also added up into imp_out [H][Lk].  With `r` the second
+// pass also produces the redundancy of the keys it holds (u from the
+// partials red_norm_sum left in the workspace) and the softmax partials of
+// r, one per key block.
+fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp_out,
                          void* ws, hipStream_t s, float* r = nullptr) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const float c = log2_scale(p);
     float2* part = at<float2>(ws, L.part);
     float* nlse2 = at<float>(ws, L.nlse2);
+    // one plane goes straight to imp_out when the caller wants importance
+    float* planes = (imp_out && L.plan.nqs == 1) ? imp_out : at<float>(ws, L.imp);
     float* u = r ? at<float>(ws, L.u) : nullptr;
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
     FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s,
                                 r ? at<float>(ws, L.u_part) : nullptr, L.nbu, u, p->d));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp, p->H, p->L_q, p->L_k, c, s, u, r,
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, c, s, u, r,
                              r ? at<float2>(ws, L.red_part) : nullptr));
+    if (imp_out && planes != imp_out) FC_TRY(launch_imp_sum_planes(planes, imp_out, p->H, p->L_k, L.plan.nqs, s));
     return FC_OK;
 }
 
@@ -159,11 +164,12 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
     float2* red_part = at<float2>(ws, L.red_part);
     // redundancy pass A: partial sums of the normalised keys
     FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, s));
-    // importance; its second pass also forms r and the softmax partials of r
-    st = run_importance(p, L, Q, K, imp, ws, s, r);
+    // importance (planes in the workspace); its second pass also forms r and
+    // the softmax partials of r
+    st = run_importance(p, L, Q, K, nullptr, ws, s, r);
     if (st != FC_OK) return st;
     // pool + score + top-B + gather
-    FC_TRY(launch_sel_head(imp, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
+    FC_TRY(launch_sel_head(imp, L.plan.nqs, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
                            at<uint32_t>(ws, L.keys), p->H, p->L_k, Bp, idx_out, s));
     FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
@@ -204,8 +210,10 @@ fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float* nlse2 = at<float>(workspace, L.nlse2);
+    float* planes = L.plan.nqs == 1 ? imp_out : at<float>(workspace, L.imp);
     FC_TRY(launch_imp_nlse2(lse, nlse2, p->H, p->L_q, s));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, imp_out, p->H, p->L_q, p->L_k, log2_scale(p), s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s));
+    if (planes != imp_out) FC_TRY(launch_imp_sum_planes(planes, imp_out, p->H, p->L_k, L.plan.nqs, s));
     return FC_OK;
 }
 
@@ -241,7 +249,7 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
     const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
     float2* red_part = at<float2>(workspace, L.red_part);
     FC_TRY(launch_red_stats(r, red_part, p->H, p->L_k, s));
-    FC_TRY(launch_sel_head(imp, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
+    FC_TRY(launch_sel_head(imp, 1, r, red_part, L.nbr, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
                            at<uint32_t>(workspace, L.keys), p->H, p->L_k, Bp, idx_out, s));
     if (gather) FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
     return FC_OK;
@@ -259,7 +267,7 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
     const size_t need = fc_topb_select_workspace_bytes(H, L);
     if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
     const int Bp = B < L ? B : L;
-    FC_TRY(launch_sel_head(scores, nullptr, nullptr, 0, 0.f, 1, nullptr, nullptr, nullptr,
+    FC_TRY(launch_sel_head(scores, 1, nullptr, nullptr, 0, 0.f, 1, nullptr, nullptr, nullptr,
                            static_cast<uint32_t*>(workspace), H, L, Bp, idx_out, static_cast<hipStream_t>(stream)));
     return FC_OK;
 }

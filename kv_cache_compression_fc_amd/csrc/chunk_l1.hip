@@ -12,7 +12,7 @@
 // forms L1_rel and updates f, the recompute flag and the step counter on the
 // device.  The kernel boundary orders the two (no cross-XCD fences or
 // atomics), and the result is deterministic.  HBM-bound: every state byte is
-// read once.
+// read once, with non-temporal loads.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -95,7 +95,10 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable t
     for (; v + (kUnroll - 1) * kThreads < nvec; v += kUnroll * kThreads) {
         uint4 xa[kUnroll], xb[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) { xa[u] = va[v + u * kThreads]; xb[u] = vb[v + u * kThreads]; }
+        for (int u = 0; u < kUnroll; ++u) {
+            xa[u] = load_stream16(va + v + u * kThreads);
+            xb[u] = load_stream16(vb + v + u * kThreads);
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) accum16<DT>(xa[u], xb[u], sa, sn);
     }

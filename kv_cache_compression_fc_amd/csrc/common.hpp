@@ -20,6 +20,18 @@ template <> struct Elem<kBF16> { using T = uint16_t; static constexpr int kBytes
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte loads and stores that bypass cache allocation (streaming data read
+// or written once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream16(void* p, const uint4& v) {
+    u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, static_cast<u32x4_t*>(p));
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -29,6 +29,7 @@
 // range's first 32 keys, and a workgroup whose sums leave the safe range (a
 // logit more than ~100 binary orders above m) redoes its range with an exact
 // running maximum.  No atomics: the result is deterministic.
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -402,6 +403,16 @@ __global__ __launch_bounds__(kSmallThreads) void imp_lse_merge_kernel(const floa
     if (nlse2) nlse2[(size_t)h * lq_pad + q] = -l2;
 }
 
+// imp[h][j] = sum of the nqs partial planes (fixed order).
+__global__ __launch_bounds__(kSmallThreads) void imp_sum_planes_kernel(const float* __restrict__ part,
+                                                                       float* __restrict__ imp, size_t n, int nqs) {
+    for (size_t i = (size_t)blockIdx.x * kSmallThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kSmallThreads) {
+        float a = part[i];
+        for (int q = 1; q < nqs; ++q) a += part[(size_t)q * n + i];
+        imp[i] = a;
+    }
+}
+
 // -lse2 padded with -inf from a natural-log lse.
 __global__ __launch_bounds__(kSmallThreads) void imp_nlse2_kernel(const float* __restrict__ lse,
                                                                   float* __restrict__ nlse2, int Lq, int lq_pad) {
@@ -462,9 +473,10 @@ template <int DT, int D>
 __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum_kernel(const void* __restrict__ Q,
                                                                                const void* __restrict__ K,
                                                                                const float* __restrict__ nlse2,
-                                                                               float* __restrict__ imp, int Lq,
-                                                                               int lq_pad, int Lk, int nkb,
-                                                                               int n_items, float c, float inv_lq,
+                                                                               float* __restrict__ imp, int H,
+                                                                               int Lq, int lq_pad, int Lk, int nkb,
+                                                                               int nqs, int tpi, int n_items,
+                                                                               float c, float inv_lq,
                                                                                const float* __restrict__ u,
                                                                                float* __restrict__ r_out,
                                                                                float2* __restrict__ red_part) {
@@ -490,9 +502,12 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         else return nl2;
     };
 
+    // item = (h * nqs + qs) * nkb + kblk: consecutive items (one XCD) share
+    // a head and a query range, so they stream the same Q tiles.
     const int item = xcd_item((n_items + 7) / 8);
     if (item >= n_items) return;
-    const int kblk = item % nkb, h = item / nkb;
+    const int kblk = item % nkb, hq = item / nkb;
+    const int qs = hq % nqs, h = hq / nqs;
 
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5;
@@ -502,22 +517,24 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
                                                  (uint32_t)Lq * D * kE);
     const __amdgpu_buffer_rsrc_t nrs = head_rsrc(nlse2 + (size_t)h * lq_pad, (uint32_t)lq_pad * 4);
     const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
-    const int ntiles = (Lq + QT - 1) / QT;
+    // this item's query tiles [t_begin, t_end)
+    const int t_begin = qs * tpi;
+    const int t_end = min((Lq + QT - 1) / QT, t_begin + tpi);
     const uint32_t tile_bytes = QT * D * kE;
 
-    // Tile t into buffer b = t % 3: Q rows (all waves share the copy) and its
+    // Tile t into buffer b = (t - t_begin) % 3: Q rows (all waves share the copy) and its
     // -lse2 (4 bytes per lane; every wave writes the same values, so the
     // per-wave load counts match and the copy needs no extra synchronisation).
     // Tiles past the last are issued with an offset outside the resources
     // (no data moves), as in imp_lse_kernel.
     auto issue = [&](auto b, int t) {
-        const bool real = t < ntiles;
+        const bool real = t < t_end;
         Tile::issue(qrs, real ? (uint32_t)t * tile_bytes : kNoRecord, lds(b), wave, lane);
         const int qi = t * QT + (lane < QT ? lane : 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(nrs, nl_lds(b), 4, real ? (uint32_t)qi * 4 : kNoRecord, 0, 0, 0);
     };
-    issue(Buf<0>{}, 0);
-    issue(Buf<1>{}, 1);  // (out of range when there is one tile)
+    issue(Buf<0>{}, t_begin);
+    issue(Buf<1>{}, t_begin + 1);  // (out of range when there is one tile)
 
     // K fragments, the register operand: key (lane%32 of the wave's 32),
     // depth 16*kk + 8*half .. +8.  They supply the rows of every product, so
@@ -529,8 +546,9 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         if (key < Lk) kf[kk].load(Kh + ((size_t)key * D + 16 * kk + 8 * half) * kE);
         else kf[kk].zero();
     }
-    if (u != nullptr) redundancy_of_keys<DT, D>(kf, u + (size_t)h * D, key, lane, Lk, r_out + (size_t)h * Lk,
-                                                 red_part + (size_t)h * nkb + kblk);
+    if (u != nullptr && qs == 0)
+        redundancy_of_keys<DT, D>(kf, u + (size_t)h * D, key, lane, Lk, r_out + (size_t)h * Lk,
+                                  red_part + (size_t)h * nkb + kblk);
     wait_vmcnt<L>();  // tile 0 landed (tile 1 may be in flight)
     tile_barrier();
 
@@ -570,15 +588,15 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
     // Whole rounds of three tiles, then the tail: the loop's back edge then
     // only follows a buffer-2 step, so the compiler sees on every path which
     // loads the explicit waits have retired and adds no waits of its own.
-    int t = 0;
-    for (; t + 2 < ntiles; t += kNBuf) {
+    int t = t_begin;
+    for (; t + 2 < t_end; t += kNBuf) {
         step(Buf<0>{}, t);
         step(Buf<1>{}, t + 1);
         step(Buf<2>{}, t + 2);
     }
-    if (t < ntiles) {
+    if (t < t_end) {
         step(Buf<0>{}, t);
-        if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
+        if (t + 1 < t_end) step(Buf<1>{}, t + 1);
     }
     wait_vmcnt<0>();
     acc_rows(carry, nl_carry, 0, 16);
@@ -594,7 +612,8 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         if ((lane & 31) == r) v = x;
     }
     const int kr = kblk * kRowsPerBlock + wave * 32 + 8 * ((lane & 15) >> 2) + 4 * half + (lane & 3);
-    if ((lane & 31) < 16 && kr < Lk) imp[(size_t)h * Lk + kr] = v * inv_lq;
+    // partial importance of this query range: plane qs of [nqs][H][Lk]
+    if ((lane & 31) < 16 && kr < Lk) imp[((size_t)qs * H + h) * Lk + kr] = v * inv_lq;
 }
 
 template <int DT, int D>
@@ -609,31 +628,100 @@ hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq,
 }
 
 template <int DT, int D>
-hipError_t colsum_launch(const void* Q, const void* K, const float* nlse2, float* imp, int H, int Lq, int Lk, float c,
-                         hipStream_t s, const float* u, float* r, float2* red_part) {
+hipError_t colsum_launch(const void* Q, const void* K, const float* nlse2, float* imp_part, int H, int Lq, int Lk,
+                         const ImpPlan& p, float c, hipStream_t s, const float* u, float* r, float2* red_part) {
     const int nkb = (Lk + kRowsPerBlock - 1) / kRowsPerBlock;
-    const long long n_items = (long long)H * nkb;
+    const long long n_items = (long long)H * p.nqs * nkb;
     const int blocks = (int)((n_items + 7) / 8 * 8);
-    hipLaunchKernelGGL((imp_colsum_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, nlse2, imp, Lq,
-                       imp_lq_pad(Lq), Lk, nkb, (int)n_items, c, 1.0f / (float)Lq, u, r, red_part);
+    hipLaunchKernelGGL((imp_colsum_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, nlse2, imp_part, H, Lq,
+                       imp_lq_pad(Lq), Lk, nkb, p.nqs, p.qtiles_per_split, (int)n_items, c, 1.0f / (float)Lq, u, r,
+                       red_part);
     return hipGetLastError();
+}
+
+// Workgroups of a kernel that fit on one CU at once (at least 1).
+template <typename Kern>
+int occupancy(Kern kern) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
+// Concurrent workgroup slots of the two importance passes on the current
+// device, cached per device and variant.
+struct Slots {
+    int lse, colsum;
+};
+Slots imp_slots(int dt, int d) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev][2][2][2];  // 0 = not computed yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+    const int di = dt == kBF16 ? 1 : 0, dd = d == 128 ? 1 : 0;
+    int a = cache[dev][di][dd][0].load(), b = cache[dev][di][dd][1].load();
+    if (a == 0 || b == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        int ol, oc;
+        if (dt == kBF16) {
+            ol = d == 128 ? occupancy(imp_lse_kernel<kBF16, 128>) : occupancy(imp_lse_kernel<kBF16, 64>);
+            oc = d == 128 ? occupancy(imp_colsum_kernel<kBF16, 128>) : occupancy(imp_colsum_kernel<kBF16, 64>);
+        } else {
+            ol = d == 128 ? occupancy(imp_lse_kernel<kF32, 128>) : occupancy(imp_lse_kernel<kF32, 64>);
+            oc = d == 128 ? occupancy(imp_colsum_kernel<kF32, 128>) : occupancy(imp_colsum_kernel<kF32, 64>);
+        }
+        a = cus * ol;
+        b = cus * oc;
+        cache[dev][di][dd][0].store(a);
+        cache[dev][di][dd][1].store(b);
+    }
+    return Slots{a, b};
+}
+
+// Split n_tiles tiles of work per (item group) into parts, choosing the
+// count that minimises (rounds of the grid) x (tiles per part + overhead):
+// a partial last round of workgroups costs a whole round.
+void choose_split(long long groups, int n_tiles, int min_tiles, int max_parts, int slots, int* parts,
+                  int* tiles_per_part) {
+    constexpr double kOverheadTiles = 2.0;  // prologue and epilogue of a workgroup, in tiles
+    int best_p = 1, best_t = n_tiles;
+    double best = 1e300;
+    int p_max = n_tiles / (min_tiles > 0 ? min_tiles : 1);
+    if (p_max < 1) p_max = 1;
+    if (p_max > max_parts) p_max = max_parts;
+    for (int p = 1; p <= p_max; ++p) {
+        const int t = (n_tiles + p - 1) / p;
+        const int p_eff = (n_tiles + t - 1) / t;  // every part non-empty
+        const long long items = groups * p_eff;
+        const long long rounds = (items + slots - 1) / slots;
+        const double cost = (double)rounds * (t + kOverheadTiles);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_p = p_eff;
+            best_t = t;
+        }
+    }
+    *parts = best_p;
+    *tiles_per_part = best_t;
 }
 
 }  // namespace
 
 int imp_lq_pad(int Lq) { return (Lq + 63) / 64 * 64; }
 
-ImpPlan imp_plan(int H, int Lq, int Lk, int dt) {
+ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d) {
     const int kt = dt == kBF16 ? tile_rows<kBF16>() : tile_rows<kF32>();
-    const long long blocks = (long long)H * ((Lq + kRowsPerBlock - 1) / kRowsPerBlock);
-    const int max_split = (Lk + 4 * kt - 1) / (4 * kt);  // keep >= 4 tiles per split
-    int ns = (int)((2048 + blocks - 1) / blocks);         // several blocks per CU: a short tail
-    if (ns > max_split) ns = max_split;
-    if (ns < 1) ns = 1;
-    int tiles = (Lk + kt - 1) / kt;
-    int kps = ((tiles + ns - 1) / ns) * kt;
-    ns = (Lk + kps - 1) / kps;  // every split non-empty
-    return ImpPlan{ns, kps};
+    const Slots sl = imp_slots(dt, d);
+    ImpPlan p{};
+    // pass 1: key ranges of whole K tiles (>= 4 tiles each)
+    int kps_tiles;
+    choose_split((long long)H * ((Lq + kRowsPerBlock - 1) / kRowsPerBlock), (Lk + kt - 1) / kt, 4, 1 << 20,
+                 sl.lse, &p.nsplit, &kps_tiles);
+    p.keys_per_split = kps_tiles * kt;
+    // pass 2: query ranges of whole Q tiles (>= 4 tiles each, at most kMaxQSplit)
+    choose_split((long long)H * ((Lk + kRowsPerBlock - 1) / kRowsPerBlock), (Lq + kt - 1) / kt, 4, kMaxQSplit,
+                 sl.colsum, &p.nqs, &p.qtiles_per_split);
+    return p;
 }
 
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq, int Lk,
@@ -646,12 +734,14 @@ hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* p
 
 int imp_colsum_blocks(int Lk) { return (Lk + kRowsPerBlock - 1) / kRowsPerBlock; }
 
-hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
-                             int Lq, int Lk, float c, hipStream_t s, const float* u, float* r, float2* red_part) {
-    if (dt == kBF16) return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part)
-                                     : colsum_launch<kBF16, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part);
-    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part)
-                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp, H, Lq, Lk, c, s, u, r, red_part);
+hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
+                             int Lq, int Lk, const ImpPlan& p, float c, hipStream_t s, const float* u, float* r,
+                             float2* red_part) {
+    if (dt == kBF16)
+        return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part)
+                        : colsum_launch<kBF16, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part);
+    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part)
+                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part);
 }
 
 hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,
@@ -659,6 +749,14 @@ hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, in
     const int lq_pad = imp_lq_pad(Lq);
     hipLaunchKernelGGL(imp_lse_merge_kernel, dim3((lq_pad + kSmallThreads - 1) / kSmallThreads, H),
                        dim3(kSmallThreads), 0, s, part, lse, nlse2, Lq, lq_pad, nsplit, u_part, nbu, u, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_imp_sum_planes(const float* part, float* imp, int H, int Lk, int nqs, hipStream_t s) {
+    const size_t n = (size_t)H * Lk;
+    size_t blocks = (n + kSmallThreads - 1) / kSmallThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(imp_sum_planes_kernel, dim3((unsigned)blocks), dim3(kSmallThreads), 0, s, part, imp, n, nqs);
     return hipGetLastError();
 }
 

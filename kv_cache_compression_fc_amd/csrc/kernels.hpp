@@ -9,26 +9,36 @@ namespace fc {
 
 // ---- importance (two passes) ----------------------------------------------
 // Pass 1 splits the keys of each head into `nsplit` ranges of
-// `keys_per_split` keys (a multiple of the key tile) to fill the machine when
-// H * ceil(L_q/128) is small; pass 2 merges the per-range (max, sum) pairs.
+// `keys_per_split` keys (whole key tiles), chosen from the device's
+// workgroup slots so that the last round of the grid is nearly full.  Pass 2
+// can split the queries into `nqs` ranges of `qtiles_per_split` query tiles,
+// one partial importance plane per range; measured on the MAGI-like shape,
+// every split costs more in per-workgroup set-up (each range re-loads its
+// keys) than it saves in the grid's last round, so the limit is one range.
+constexpr int kMaxQSplit = 1;
 struct ImpPlan {
     int nsplit;
     int keys_per_split;
+    int nqs;
+    int qtiles_per_split;
 };
-ImpPlan imp_plan(int H, int Lq, int Lk, int dt);
+ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d);
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
                           int Lk, const ImpPlan& plan, float c, hipStream_t s);
 // Queries padded to whole pass-2 tiles.
 int imp_lq_pad(int Lq);
 // Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled
-// logits, negated, padded with -inf).  With u != nullptr ([H][d], the sum of
-// the normalised keys) pass 2 also writes the redundancy r [H][Lk] of the
-// keys it holds and one softmax partial (max, sum e^{r-max}, base 2) per
-// workgroup into red_part [H][imp_colsum_blocks(Lk)].
+// logits, negated, padded with -inf) into imp_part [nqs][H][Lk] (the planes
+// add up to the importance).  With u != nullptr ([H][d], the sum of the
+// normalised keys) pass 2 also writes the redundancy r [H][Lk] of the keys
+// it holds and one softmax partial (max, sum e^{r-max}, base 2) per key
+// block into red_part [H][imp_colsum_blocks(Lk)].
 int imp_colsum_blocks(int Lk);
-hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp, int H,
-                             int Lq, int Lk, float c, hipStream_t s, const float* u = nullptr,
+hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
+                             int Lq, int Lk, const ImpPlan& plan, float c, hipStream_t s, const float* u = nullptr,
                              float* r = nullptr, float2* red_part = nullptr);
+// imp [H][Lk] = the sum of the nqs planes of imp_part.
+hipError_t launch_imp_sum_planes(const float* imp_part, float* imp, int H, int Lk, int nqs, hipStream_t s);
 // From the pass-1 partials: the natural-log lse [H][Lq] and/or -lse2 (either
 // may be nullptr).  With u_part != nullptr it also sums the redundancy
 // partials u_part [H][nbu][d] into u [H][d].
@@ -37,7 +47,6 @@ hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, in
                                 int d = 0);
 // -lse2 from a natural-log lse.
 hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipStream_t s);
-
 // ---- redundancy -------------------------------------------------------------
 // Blocks per head of the two redundancy passes.
 int red_nbu(int Lk);
@@ -55,9 +64,11 @@ hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, hip
 // else `src` holds them), order-preserving keys (spilled to keys [H][L] when a
 // head exceeds one chunk), radix select of the B' largest and the ordered
 // compaction into idx_out [H][Bp].
-hipError_t launch_sel_head(const float* src, const float* r, const float2* red_part, int nbr, float lam, int w,
-                           float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H, int L,
-                           int Bp, int32_t* idx_out, hipStream_t s);
+// With r != nullptr, `src` holds nsrc planes [nsrc][H][L] of importance that
+// add up to it.
+hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
+                           int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
+                           int L, int Bp, int32_t* idx_out, hipStream_t s);
 // K_out[h][b] = K[h][idx[h][b]], V likewise.
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
                          void* K_out, void* V_out, hipStream_t s);

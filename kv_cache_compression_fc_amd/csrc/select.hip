@@ -109,11 +109,12 @@ __device__ __forceinline__ uint32_t find_bin_from_top(const uint32_t* hist, uint
     return b;
 }
 
-// kFromImp: scores from importance (pooled here) and redundancy r with its
-// softmax partials red_part [H][nbr]; otherwise `src` holds the scores.
+// kFromImp: scores from importance (nsrc planes [nsrc][H][L] that add up to
+// it; pooled here) and redundancy r with its softmax partials red_part
+// [H][nbr]; otherwise `src` holds the scores.
 template <bool kFromImp>
 __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
-    const float* __restrict__ src, const float* __restrict__ r, const float2* __restrict__ red_part, int nbr,
+    const float* __restrict__ src, int nsrc, const float* __restrict__ r, const float2* __restrict__ red_part, int nbr,
     float lam, int hw, float* __restrict__ score_out, float* __restrict__ imp_pooled_out,
     float* __restrict__ red_out, uint32_t* __restrict__ keys, int L, int Bp, int32_t* __restrict__ idx_out) {
     // Area A: the chunk's importance with its halo (tile_a[kMaxHalo + x] =
@@ -171,13 +172,22 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
             for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = __float_as_uint(v[q]);
         }
         if constexpr (kFromImp) {
-            // importance with a halo of hw <= kMaxHalo on each side
+            // importance with a halo of hw <= kMaxHalo on each side (the
+            // planes added in a fixed order)
             constexpr int kQa = (kChunk + 2 * kMaxHalo + kSelThreads - 1) / kSelThreads;
+            const size_t plane = (size_t)gridDim.x * L;
             float v[kQa];
 #pragma unroll
             for (int q = 0; q < kQa; ++q) {
                 const int i = tid + q * kSelThreads, j = c0 - hw + i;
                 v[q] = (i < kChunk + 2 * hw && j >= 0 && j < L) ? src[hL + j] : -INFINITY;
+            }
+            for (int pl = 1; pl < nsrc; ++pl) {
+#pragma unroll
+                for (int q = 0; q < kQa; ++q) {
+                    const int i = tid + q * kSelThreads, j = c0 - hw + i;
+                    if (i < kChunk + 2 * hw && j >= 0 && j < L) v[q] += src[pl * plane + hL + j];
+                }
             }
 #pragma unroll
             for (int q = 0; q < kQa; ++q) {
@@ -343,7 +353,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
 }
 
 // K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
-// kRowBytes/16 lanes, kGatherRows output rows per block.
+// kRowBytes/16 lanes, kGatherRows output rows per block.  Rows are read and
+// written once, with non-temporal accesses.
 constexpr int kThreads = 256;
 constexpr int kGatherRows = 64;
 
@@ -372,16 +383,16 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
         if ((unsigned)j[i] < (unsigned)L) {
-            kv[i] = *reinterpret_cast<const uint4*>(Ks + (size_t)j[i] * kRowBytes);
-            vv[i] = *reinterpret_cast<const uint4*>(Vs + (size_t)j[i] * kRowBytes);
+            kv[i] = load_stream16(Ks + (size_t)j[i] * kRowBytes);
+            vv[i] = load_stream16(Vs + (size_t)j[i] * kRowBytes);
         }
     }
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
         if ((unsigned)j[i] < (unsigned)L) {
             const size_t b = (size_t)(b0 + i * kRpi);
-            *reinterpret_cast<uint4*>(Kd + b * kRowBytes) = kv[i];
-            *reinterpret_cast<uint4*>(Vd + b * kRowBytes) = vv[i];
+            store_stream16(Kd + b * kRowBytes, kv[i]);
+            store_stream16(Vd + b * kRowBytes, vv[i]);
         }
     }
 }
@@ -396,15 +407,15 @@ hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K
 
 }  // namespace
 
-hipError_t launch_sel_head(const float* src, const float* r, const float2* red_part, int nbr, float lam, int w,
-                           float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H, int L,
-                           int Bp, int32_t* idx_out, hipStream_t s) {
+hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
+                           int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
+                           int L, int Bp, int32_t* idx_out, hipStream_t s) {
     if (r != nullptr)
-        hipLaunchKernelGGL(sel_head_kernel<true>, dim3(H), dim3(kSelThreads), 0, s, src, r, red_part, nbr, lam,
+        hipLaunchKernelGGL(sel_head_kernel<true>, dim3(H), dim3(kSelThreads), 0, s, src, nsrc, r, red_part, nbr, lam,
                            (w - 1) / 2, score_out, imp_pooled_out, red_out, keys, L, Bp, idx_out);
     else
-        hipLaunchKernelGGL(sel_head_kernel<false>, dim3(H), dim3(kSelThreads), 0, s, src, nullptr, nullptr, 0, 0.f,
-                           0, nullptr, nullptr, nullptr, keys, L, Bp, idx_out);
+        hipLaunchKernelGGL(sel_head_kernel<false>, dim3(H), dim3(kSelThreads), 0, s, src, 1, nullptr, nullptr, 0,
+                           0.f, 0, nullptr, nullptr, nullptr, keys, L, Bp, idx_out);
     return hipGetLastError();
 }
 
