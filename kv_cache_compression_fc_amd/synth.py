@@ -243,3 +243,92 @@ class ChunkTrajectory:
             xt[s:e] = self.state(i, t)
             xtm1[s:e] = self.state(i, t - 1)
         return xt, xtm1, steps
+
+
+# ---------------------------------------------------------------------------
+# Multi-chunk runs of the KV cache (a chunk completes, its keys join the cache)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class CacheConfig:
+    name: str
+    H: int
+    d: int
+    n_chunks: int          # chunks committed, oldest first
+    fpc: int               # latent frames per chunk
+    ny: int
+    nx: int
+    B_budget: int          # clean tokens each head keeps
+    B_active: int          # tokens of one chunk (the denoising region)
+    Lq: int                # queries that score each compression
+    lam: float
+    w: int
+    dtype: str
+    sigma: float = 3.0
+    noise: float = 0.1
+
+    @property
+    def tokens_per_chunk(self) -> int:
+        return self.fpc * self.ny * self.nx
+
+
+CACHE_CONFIGS = {
+    # Small: 2 heads, d=64, chunks of 2 frames x 8 x 6 = 96 tokens, a budget of
+    # 160 tokens (the cache overflows from the second chunk on), fp32.
+    "tiny": CacheConfig("tiny", H=2, d=64, n_chunks=6, fpc=2, ny=8, nx=6, B_budget=160, B_active=96, Lq=96,
+                        lam=0.5, w=5, dtype="f32"),
+    # MAGI-1-like run: 24 heads, d=128, chunks of 4 latent frames of 30 x 30
+    # (3600 tokens), a budget of two chunks (7200), the active chunk's 3600
+    # queries, ten chunks.  Every commit from the third on merges 10800 tokens
+    # and keeps 7200.
+    "magi": CacheConfig("magi", H=24, d=128, n_chunks=10, fpc=4, ny=30, nx=30, B_budget=7200, B_active=3600,
+                        Lq=3600, lam=0.5, w=7, dtype="bf16"),
+}
+
+
+def cache_inputs(cfg: CacheConfig, seed: int = 0, heads: Optional[Sequence[int]] = None):
+    """Keys and values of every chunk of the run and the queries of every
+    commit, as CPU tensors in the storage dtype:
+      K, V  [H'][n_chunks * T][d]   (chunk c = rows [c T, (c+1) T), T tokens per chunk)
+      Q     [n_chunks][H'][Lq][d]   (the queries that score commit c)
+    Keys are one smooth random field over the whole video, so neighbouring
+    chunks are correlated as consecutive frames are."""
+    T = cfg.tokens_per_chunk
+    frames = cfg.n_chunks * cfg.fpc
+    kcfg = KVConfig(cfg.name, H=cfg.H, d=cfg.d, Lq=cfg.Lq, Lk=cfg.n_chunks * T, B=cfg.B_budget, lam=(cfg.lam,),
+                    w=cfg.w, dtype=cfg.dtype, key_kind="field", frames=frames, ny=cfg.ny, nx=cfg.nx,
+                    sigma=cfg.sigma, noise=cfg.noise)
+    _, K, V = kv_inputs(kcfg, seed, heads)
+    if heads is None:
+        heads = range(cfg.H)
+    heads = list(heads)
+    q_ss = np.random.SeedSequence([seed, 1]).spawn(cfg.n_chunks)
+    Q = np.empty((cfg.n_chunks, len(heads), cfg.Lq, cfg.d), np.float32)
+    for c in range(cfg.n_chunks):
+        per_head = q_ss[c].spawn(cfg.H)
+        for n, h in enumerate(heads):
+            Q[c, n] = np.random.default_rng(per_head[h]).standard_normal((cfg.Lq, cfg.d), dtype=np.float32)
+    return _to_storage(Q, cfg.dtype), K, V
+
+
+def group_labels(H: int, n_chunks: int, T: int, seed: int, spread: int = 3) -> np.ndarray:
+    """int64 [H][n_chunks * T]: each token of chunk c draws its group from
+    {c, c-1, ..., c-spread+1} (clipped at 0), so groups have varied sizes and
+    later chunks repeat earlier ones."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 2]))
+    g = np.empty((H, n_chunks * T), np.int64)
+    for c in range(n_chunks):
+        lo = max(0, c - spread + 1)
+        g[:, c * T:(c + 1) * T] = rng.integers(lo, c + 1, size=(H, T))
+    return g
+
+
+def group_keys(groups: np.ndarray, d: int, dtype: str, scale: float = 1.0) -> torch.Tensor:
+    """Keys [H][L][d] with k[h][j] = scale * e_{groups[h][j]} (unit vectors):
+    keys of one group are exact duplicates, keys of different groups are
+    orthogonal."""
+    H, L = groups.shape
+    assert int(groups.max()) < d
+    K = np.zeros((H, L, d), np.float32)
+    K[np.arange(H)[:, None], np.arange(L)[None, :], groups] = scale
+    return _to_storage(K, dtype)

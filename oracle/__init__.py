@@ -22,7 +22,11 @@ Video Generation" (papernotes.org ICLR 2026 digest), section 方法详解 /
   of l2-normalised keys and a zeroed diagonal;
   Score_j = lambda * Imp~_j - (1 - lambda) * Red_j; each head keeps its top-B
   tokens.  The flowchart under 整体框架 ("Overall framework") shows the same
-  two parts and the "cache full -> score, keep top-B per head" step.
+  two parts and the "cache full -> score, keep top-B per head" step;
+* the cache manager of item 3: a fixed buffer split into a compressed clean
+  region of B_budget tokens and the denoising region; a completed chunk is
+  merged into the clean tokens and, when they no longer fit, compressed back
+  to B_budget.
 
 Readings where the page leaves a step open (each is also listed in the design
 notes of the repository):
@@ -38,7 +42,11 @@ notes of the repository):
   B' = min(B, L_k) (L_k <= B keeps every token);
 * V follows K: the same indices select both;
 * forced steps count from each chunk's own first step; f = 0 during them;
-  ">" recomputes and "<=" reuses; ||X_t||_1 = 0 gives L1_rel = +inf.
+  ">" recomputes and "<=" reuses; ||X_t||_1 = 0 gives L1_rel = +inf;
+* cache "full": the clean tokens plus the completed chunk exceed B_budget;
+  the merged order is clean tokens (as kept) then the chunk, and the pool
+  runs along that order; the queries that score a compression are the
+  caller's.
 """
 from __future__ import annotations
 
@@ -262,3 +270,43 @@ def decide(n: int, f: float, l1_rel: float, m: int, eps: float) -> Tuple[bool, f
     if a > eps:
         return True, 0.0
     return False, a
+
+
+# ---------------------------------------------------------------------------
+# KV cache manager (flowchart under 整体框架; Key designs, item 3)
+# ---------------------------------------------------------------------------
+
+def cache_merge(K_clean, V_clean, pos_clean: np.ndarray, K_chunk, V_chunk, pos0: int):
+    """A completed chunk enters the cache: per head, the clean tokens (oldest
+    first, as kept) followed by the chunk's tokens, whose positions are
+    pos0, pos0 + 1, ...  K and V are torch CPU tensors [H][L][d] (their values
+    are kept exactly); positions int64 [H][L]."""
+    import torch
+    H, Lc = K_chunk.shape[0], K_chunk.shape[1]
+    K = torch.cat([K_clean, K_chunk], dim=1)
+    V = torch.cat([V_clean, V_chunk], dim=1)
+    new_pos = np.broadcast_to(pos0 + np.arange(Lc, dtype=np.int64), (H, Lc))
+    pos = np.concatenate([np.asarray(pos_clean, np.int64).reshape(H, -1), new_pos], axis=1)
+    return K, V, pos
+
+
+def cache_commit(K_clean, V_clean, pos_clean, K_chunk, V_chunk, pos0: int, Q, B_budget: int, lam: float, w: int,
+                 scale: Optional[float] = None) -> Dict[str, object]:
+    """One commit of a completed chunk into the clean region of B_budget
+    tokens per head.
+
+    The flowchart's branch: when the merged tokens fit the budget the cache is
+    not full and every token is kept as is; otherwise the merged set is
+    scored with the queries Q and each head keeps its top-B_budget tokens
+    (kv_compress), in ascending merged order, so the cache stays in temporal
+    order.  Returns the new K, V, positions, and, after a compression, the
+    compression's intermediate values ("comp", merged indices in comp["idx"])
+    and the merged set ("merged": K, V, pos).
+    """
+    Km, Vm, pm = cache_merge(K_clean, V_clean, pos_clean, K_chunk, V_chunk, pos0)
+    if Km.shape[1] <= B_budget:
+        return {"K": Km, "V": Vm, "pos": pm, "comp": None, "merged": (Km, Vm, pm)}
+    comp = kv_compress(Q, Km, Vm, B_budget, lam, w, scale)
+    idx = comp["idx"]
+    pos = np.stack([pm[h][idx[h]] for h in range(pm.shape[0])])
+    return {"K": comp["K_out"], "V": comp["V_out"], "pos": pos, "comp": comp, "merged": (Km, Vm, pm)}

@@ -202,11 +202,11 @@ def test_importance_two_stages(fc, dtype, d, H, Lq, Lk):
     assert parity.max_rel_err(imp.cpu().numpy(), oracle.importance(Q, K, 1 / math.sqrt(d))) <= parity.REL
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_importance_wide_logit_range(fc, dtype):
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 64), ("bf16", 128)])
+def test_importance_wide_logit_range(fc, dtype, d):
     # a later key scores ~150 binary orders above the first keys of its range,
     # which the fixed shift of pass 1 cannot hold: the exact path must take over
-    H, Lq, Lk, d = 2, 70, 700, 64
+    H, Lq, Lk = 2, 70, 700
     rng = np.random.default_rng(13)
     Q = rng.standard_normal((H, Lq, d)).astype(np.float32)
     K = 0.01 * rng.standard_normal((H, Lk, d)).astype(np.float32)
@@ -216,7 +216,7 @@ def test_importance_wide_logit_range(fc, dtype):
     Qt, Kt = torch.from_numpy(Q), torch.from_numpy(K)
     if dtype == "bf16":
         Qt, Kt = Qt.to(torch.bfloat16), Kt.to(torch.bfloat16)
-    say(f"case: importance with a 100-nat logit spread ({dtype})")
+    say(f"case: importance with a 100-nat logit spread ({dtype}, d={d})")
     imp = fc.fc_kv_importance(Qt.to(DEV), Kt.to(DEV), softmax_scale=1.0)
     lse = fc.fc_kv_importance_lse(Qt.to(DEV), Kt.to(DEV), softmax_scale=1.0)
     torch.cuda.synchronize()
