@@ -174,6 +174,66 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* KV cache manager (Key designs item 3; flowchart under 整体框架)          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The page splits a fixed KV buffer B_total into a compressed clean region of
+ * B_budget tokens and the region of the chunk being denoised (B_active).
+ * When a chunk completes it enters the cache; if the clean tokens and the
+ * chunk together exceed B_budget ("cache full"), the merged set is compressed
+ * back to B_budget tokens per head with the joint score above; otherwise the
+ * chunk is kept as it is.
+ *
+ *   H, d, lambda, pool_window, softmax_scale, dtype   as in fc_kv_params
+ *   B_budget   clean tokens each head keeps
+ *   B_active   most tokens one committed chunk may bring (per head)
+ */
+typedef struct {
+    int32_t H, d, B_budget, B_active;
+    float lambda;
+    int32_t pool_window;
+    float softmax_scale;
+    fc_dtype dtype;
+} fc_cache_params;
+
+/* Workspace bytes that fc_cache_commit needs for any commit scored by L_q
+ * queries (0 if the parameters are invalid).  A commit that does not
+ * compress needs no workspace. */
+size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q);
+
+/*
+ * fc_cache_commit -- a completed chunk enters the cache.
+ *   L_clean          host int32 in/out: clean tokens per head before the call
+ *                    (0..B_budget); after it, min(L_clean + L_c, B_budget)
+ *   K_chunk, V_chunk [H][L_c][d] device, dtype: the chunk's keys and values,
+ *                    1 <= L_c <= B_active
+ *   pos0             position of the chunk's first token (its tokens get
+ *                    pos0, pos0 + 1, ...; pos0 >= 0, pos0 + L_c <= 2^31 - 1)
+ *   Q [H][L_q][d]    device, dtype: the queries that score a compression;
+ *                    may be NULL when the chunk fits (no compression)
+ *   K_clean, V_clean [H][B_budget][d] device, dtype, in/out: the clean
+ *                    region; head h's tokens are rows 0..L_clean-1 of its
+ *                    B_budget rows, in ascending position order
+ *   pos_clean        [H][B_budget] int32 device in/out, nullable: the
+ *                    positions of the clean tokens
+ * Not full (L_clean + L_c <= B_budget): the chunk's rows are copied behind
+ * the clean rows.  Full: the merged set (clean rows, then the chunk) is
+ * compressed as by fc_kv_compress with L_k = L_clean + L_c into the clean
+ * region, and the positions follow the kept rows.  The workspace (device,
+ * >= the query for this L_q) holds the merged set; it may be NULL for a
+ * commit that does not compress.  K_chunk, V_chunk and Q must not overlap
+ * the clean region.  *L_clean is updated when the work has been queued.
+ * Errors as for fc_kv_compress; an L_clean, L_c or pos0 out of range, or a
+ * NULL Q for a commit that compresses, is FC_ERR_INVALID_ARG.
+ */
+fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean,
+                          const void* K_chunk, const void* V_chunk, int32_t L_c, int32_t pos0,
+                          const void* Q, int32_t L_q,
+                          void* K_clean, void* V_clean, int32_t* pos_clean,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Chunkwise relative L1 and reuse decision (Key designs, items 1 and 2)    */
 /* ------------------------------------------------------------------------ */
 

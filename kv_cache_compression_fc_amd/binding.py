@@ -34,6 +34,7 @@ EXPORTS = (
     "fc_kv_importance_lse", "fc_kv_importance_colsum",
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
     "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
+    "fc_cache_commit_workspace_bytes", "fc_cache_commit",
 )
 
 
@@ -42,6 +43,12 @@ class fc_kv_params(ctypes.Structure):
                 ("L_k", ctypes.c_int32), ("B_budget", ctypes.c_int32), ("lambda_", ctypes.c_float),
                 ("pool_window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("dtype", ctypes.c_int)]
+
+
+class fc_cache_params(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("B_budget", ctypes.c_int32),
+                ("B_active", ctypes.c_int32), ("lambda_", ctypes.c_float), ("pool_window", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int)]
 
 
 class fc_l1_params(ctypes.Structure):
@@ -76,6 +83,12 @@ _lib.fc_chunk_rel_l1_workspace_bytes.argtypes = [ctypes.POINTER(fc_l1_params), _
 _lib.fc_chunk_rel_l1_decide.restype = ctypes.c_int
 _lib.fc_chunk_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]
+
+_lib.fc_cache_commit_workspace_bytes.restype = _sz
+_lib.fc_cache_commit_workspace_bytes.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.c_int32]
+_lib.fc_cache_commit.restype = ctypes.c_int
+_lib.fc_cache_commit.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.POINTER(ctypes.c_int32), _vp, _vp,
+                                 ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp]
 
 
 class FlowCacheError(RuntimeError):
@@ -277,3 +290,46 @@ def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X
     _check("fc_chunk_rel_l1_decide", _lib.fc_chunk_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
         _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def fc_cache_commit_workspace_bytes(c: fc_cache_params, L_q: int) -> int:
+    return int(_lib.fc_cache_commit_workspace_bytes(ctypes.byref(c), int(L_q)))
+
+
+def fc_cache_commit(c: fc_cache_params, L_clean: int, K_chunk, V_chunk, pos0: int, Q, K_clean, V_clean,
+                    pos_clean=None, workspace=None, stream=None) -> int:
+    """One commit; returns the new clean length."""
+    n = ctypes.c_int32(int(L_clean))
+    L_q = int(Q.shape[1]) if Q is not None else 0
+    _check("fc_cache_commit", _lib.fc_cache_commit(
+        ctypes.byref(c), ctypes.byref(n), _ptr(K_chunk), _ptr(V_chunk), int(K_chunk.shape[1]), int(pos0), _ptr(Q),
+        L_q, _ptr(K_clean), _ptr(V_clean), _ptr(pos_clean), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return int(n.value)
+
+
+class KvCache:
+    """A fixed-size KV cache on the device: the clean region K, V
+    [H][B_budget][d], the tokens' positions [H][B_budget] and the commit
+    workspace, allocated once.  ``commit`` adds a completed chunk (its tokens
+    take the next positions) and compresses when the budget overflows."""
+
+    def __init__(self, H: int, d: int, B_budget: int, B_active: int, L_q: int, lam: float, pool_window: int,
+                 dtype: torch.dtype, softmax_scale: float = 0.0, device="cuda"):
+        self.p = fc_cache_params(int(H), int(d), int(B_budget), int(B_active), float(lam), int(pool_window),
+                                 float(softmax_scale), FC_BF16 if dtype == torch.bfloat16 else FC_F32)
+        nbytes = fc_cache_commit_workspace_bytes(self.p, L_q)
+        if nbytes == 0:
+            raise FlowCacheError("fc_cache_commit_workspace_bytes", FC_ERR_INVALID_ARG)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.K = torch.zeros((H, B_budget, d), dtype=dtype, device=device)
+        self.V = torch.zeros_like(self.K)
+        self.pos = torch.full((H, B_budget), -1, dtype=torch.int32, device=device)
+        self.length = 0        # clean tokens per head
+        self.next_pos = 0      # position of the next committed token
+
+    def commit(self, K_chunk, V_chunk, Q=None, stream=None) -> int:
+        self.length = fc_cache_commit(self.p, self.length, K_chunk, V_chunk, self.next_pos, Q, self.K, self.V,
+                                      self.pos, self.workspace, stream)
+        self.next_pos += int(K_chunk.shape[1])
+        return self.length

@@ -100,6 +100,72 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     return FC_OK;
 }
 
+// The whole compression of K, V [H][L_k][d] into K_out, V_out [H][B'][d]
+// (arguments already checked).  With pos_out the positions pos [H][L_k]
+// follow the kept rows.
+fc_status kv_compress_run(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, const void* V,
+                          void* K_out, void* V_out, int32_t* idx_out, float* score_out, float* imp_pooled_out,
+                          float* red_out, void* ws, hipStream_t s, const int32_t* pos = nullptr,
+                          int32_t* pos_out = nullptr) {
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
+    float* imp = at<float>(ws, L.imp);
+    float* r = at<float>(ws, L.r);
+    float2* red_part = at<float2>(ws, L.red_part);
+    // redundancy pass A: partial sums of the normalised keys
+    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, s));
+    // importance (planes in the workspace); its second pass also forms r and
+    // the softmax partials of r
+    const fc_status st = run_importance(p, L, Q, K, nullptr, ws, s, r);
+    if (st != FC_OK) return st;
+    // pool + score + top-B + gather
+    FC_TRY(launch_sel_head(imp, L.plan.nqs, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out,
+                           red_out, at<uint32_t>(ws, L.keys), p->H, p->L_k, Bp, idx_out, s));
+    FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out));
+    return FC_OK;
+}
+
+// ---- KV cache manager ----------------------------------------------------------------------
+fc_status check_cache(const fc_cache_params* c) {
+    if (c == nullptr) return FC_ERR_INVALID_ARG;
+    if (c->H < 1 || c->d < 1 || c->B_budget < 1 || c->B_active < 1) return FC_ERR_INVALID_ARG;
+    if ((long long)c->B_budget + c->B_active > 0x7fffffffLL) return FC_ERR_UNSUPPORTED;
+    return FC_OK;
+}
+
+// Compression parameters of a commit that merges L tokens.
+fc_kv_params cache_kv_params(const fc_cache_params* c, int32_t L_q, int32_t L) {
+    fc_kv_params p{};
+    p.H = c->H;
+    p.d = c->d;
+    p.L_q = L_q;
+    p.L_k = L;
+    p.B_budget = c->B_budget;
+    p.lambda = c->lambda;
+    p.pool_window = c->pool_window;
+    p.softmax_scale = c->softmax_scale;
+    p.dtype = c->dtype;
+    return p;
+}
+
+// Workspace of a compressing commit: the merged set (K, V, positions), the
+// kept indices, then the compression's own workspace.
+struct CacheLayout {
+    size_t Km, Vm, pm, idx, comp;
+};
+CacheLayout cache_layout(const fc_cache_params* c) {
+    const size_t H = (size_t)c->H, Bt = (size_t)c->B_budget + (size_t)c->B_active;
+    const size_t row = (size_t)c->d * (c->dtype == FC_BF16 ? 2 : 4);
+    CacheLayout L{};
+    size_t o = 0;
+    L.Km = o;   o = align_up(o + H * Bt * row);
+    L.Vm = o;   o = align_up(o + H * Bt * row);
+    L.pm = o;   o = align_up(o + H * Bt * sizeof(int32_t));
+    L.idx = o;  o = align_up(o + H * (size_t)c->B_budget * sizeof(int32_t));
+    L.comp = o;
+    return L;
+}
+
 // ---- chunk L1 ------------------------------------------------------------------------------
 fc_status chunk_table(const fc_l1_params* p, const int64_t* off, ChunkTable* tab) {
     if (p == nullptr || off == nullptr) return FC_ERR_INVALID_ARG;
@@ -155,24 +221,8 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
         return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
     if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
-    const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
-    void* ws = workspace;
-    float* imp = at<float>(ws, L.imp);
-    float* r = at<float>(ws, L.r);
-    float2* red_part = at<float2>(ws, L.red_part);
-    // redundancy pass A: partial sums of the normalised keys
-    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, s));
-    // importance (planes in the workspace); its second pass also forms r and
-    // the softmax partials of r
-    st = run_importance(p, L, Q, K, nullptr, ws, s, r);
-    if (st != FC_OK) return st;
-    // pool + score + top-B + gather
-    FC_TRY(launch_sel_head(imp, L.plan.nqs, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out, red_out,
-                           at<uint32_t>(ws, L.keys), p->H, p->L_k, Bp, idx_out, s));
-    FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s));
-    return FC_OK;
+    return kv_compress_run(p, L, Q, K, V, K_out, V_out, idx_out, score_out, imp_pooled_out, red_out, workspace,
+                           static_cast<hipStream_t>(stream));
 }
 
 fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, float* imp_out, void* workspace,
@@ -269,6 +319,66 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
     const int Bp = B < L ? B : L;
     FC_TRY(launch_sel_head(scores, 1, nullptr, nullptr, 0, 0.f, 1, nullptr, nullptr, nullptr,
                            static_cast<uint32_t*>(workspace), H, L, Bp, idx_out, static_cast<hipStream_t>(stream)));
+    return FC_OK;
+}
+
+size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q) {
+    if (check_cache(c) != FC_OK || L_q < 1) return 0;
+    // the compression's workspace for every merged length B_budget < L <= B_total;
+    // it changes with L only through whole tiles of keys (32 or 64 rows), so one
+    // length per 32 rows and the largest length cover every case
+    const int32_t lo = c->B_budget + 1, hi = c->B_budget + c->B_active;
+    size_t comp = 0;
+    for (long long L = lo;; L = (L / 32 + 1) * 32) {
+        const int32_t Lk = (int32_t)(L < hi ? L : hi);
+        const fc_kv_params p = cache_kv_params(c, L_q, Lk);
+        if (check_kv(&p) != FC_OK) return 0;
+        const size_t t = kv_layout(&p).total;
+        comp = t > comp ? t : comp;
+        if (Lk >= hi) break;
+    }
+    return cache_layout(c).comp + comp;
+}
+
+fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void* K_chunk, const void* V_chunk,
+                          int32_t L_c, int32_t pos0, const void* Q, int32_t L_q, void* K_clean, void* V_clean,
+                          int32_t* pos_clean, void* workspace, size_t workspace_bytes, void* stream) {
+    fc_status st = check_cache(c);
+    if (st != FC_OK) return st;
+    if (L_clean == nullptr || *L_clean < 0 || *L_clean > c->B_budget) return FC_ERR_INVALID_ARG;
+    if (L_c < 1 || L_c > c->B_active || pos0 < 0 || (long long)pos0 + L_c > 0x7fffffffLL) return FC_ERR_INVALID_ARG;
+    if (!K_chunk || !V_chunk || !K_clean || !V_clean) return FC_ERR_INVALID_ARG;
+    if (!aligned16(K_chunk) || !aligned16(V_chunk) || !aligned16(K_clean) || !aligned16(V_clean))
+        return FC_ERR_INVALID_ARG;
+    const int32_t n_old = *L_clean, L = n_old + L_c;
+    // the compression's checks (head dim, dtype, lambda, window, scale, sizes)
+    // apply to every commit, so that an invalid cache fails on its first call
+    const fc_kv_params kp = cache_kv_params(c, L_q > 0 ? L_q : 1, L);
+    st = check_kv(&kp);
+    if (st != FC_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int dt = c->dtype == FC_BF16 ? kBF16 : kF32;
+    if (L <= c->B_budget) {
+        // not full: the chunk is kept as it is, behind the clean tokens
+        FC_TRY(launch_cache_rows(dt, c->d, c->H, nullptr, nullptr, nullptr, 0, 0, K_chunk, V_chunk, L_c, pos0,
+                                 K_clean, V_clean, pos_clean, c->B_budget, n_old, s));
+        *L_clean = L;
+        return FC_OK;
+    }
+    // full: merge, then keep the top-B_budget tokens of the merged set per head
+    if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
+    const CacheLayout CL = cache_layout(c);
+    const KvLayout KL = kv_layout(&kp);
+    if (workspace == nullptr || workspace_bytes < CL.comp + KL.total) return FC_ERR_WORKSPACE;
+    void* Km = at<char>(workspace, CL.Km);
+    void* Vm = at<char>(workspace, CL.Vm);
+    int32_t* pm = pos_clean ? at<int32_t>(workspace, CL.pm) : nullptr;
+    FC_TRY(launch_cache_rows(dt, c->d, c->H, K_clean, V_clean, pos_clean, c->B_budget, n_old, K_chunk, V_chunk, L_c,
+                             pos0, Km, Vm, pm, L, 0, s));
+    st = kv_compress_run(&kp, KL, Q, Km, Vm, K_clean, V_clean, at<int32_t>(workspace, CL.idx), nullptr, nullptr,
+                         nullptr, at<char>(workspace, CL.comp), s, pm, pos_clean);
+    if (st != FC_OK) return st;
+    *L_clean = c->B_budget;
     return FC_OK;
 }
 

@@ -69,9 +69,20 @@ hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, hip
 hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
                            int L, int Bp, int32_t* idx_out, hipStream_t s);
-// K_out[h][b] = K[h][idx[h][b]], V likewise.
+// K_out[h][b] = K[h][idx[h][b]], V likewise; with pos_out also
+// pos_out[h][b] = pos[h][idx[h][b]] (pos [H][L], pos_out [H][Bp]).
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
-                         void* K_out, void* V_out, hipStream_t s);
+                         void* K_out, void* V_out, hipStream_t s, const int32_t* pos = nullptr,
+                         int32_t* pos_out = nullptr);
+
+// ---- KV cache manager -----------------------------------------------------------
+// dst[h][row0 + j] = j < n_old ? old[h][j] : fresh[h][j - n_old] for K and V,
+// 0 <= j < n_old + n_new, head strides ld_old / n_new / ld_dst rows; with
+// pos_dst also the positions (pos_old[h][j] for old rows, pos0 + j - n_old
+// for fresh ones).
+hipError_t launch_cache_rows(int dt, int d, int H, const void* K_old, const void* V_old, const int32_t* pos_old,
+                             int ld_old, int n_old, const void* K_new, const void* V_new, int n_new, int32_t pos0,
+                             void* K_dst, void* V_dst, int32_t* pos_dst, int ld_dst, int row0, hipStream_t s);
 
 // ---- chunk relative L1 ------------------------------------------------------
 constexpr int kMaxChunks = 128;

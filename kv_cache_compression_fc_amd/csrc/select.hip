@@ -354,14 +354,17 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
 
 // K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
 // kRowBytes/16 lanes, kGatherRows output rows per block.  Rows are read and
-// written once, with non-temporal accesses.
+// written once, with non-temporal accesses.  With pos_out, the tokens'
+// positions follow them: pos_out[h][b] = pos[h][idx[h][b]].
 constexpr int kThreads = 256;
 constexpr int kGatherRows = 64;
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __restrict__ idx, int L, int Bp,
                                                                const void* __restrict__ K, const void* __restrict__ V,
-                                                               void* __restrict__ K_out, void* __restrict__ V_out) {
+                                                               void* __restrict__ K_out, void* __restrict__ V_out,
+                                                               const int32_t* __restrict__ pos,
+                                                               int32_t* __restrict__ pos_out) {
     constexpr int kRowBytes = D * Elem<DT>::kBytes;
     constexpr int kTpr = kRowBytes / 16;     // lanes per row
     constexpr int kRpi = kThreads / kTpr;    // rows per step
@@ -393,15 +396,17 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __
             const size_t b = (size_t)(b0 + i * kRpi);
             store_stream16(Kd + b * kRowBytes, kv[i]);
             store_stream16(Vd + b * kRowBytes, vv[i]);
+            if (pos_out != nullptr && e == 0) pos_out[(size_t)h * Bp + b] = pos[(size_t)h * L + j[i]];
         }
     }
 }
 
 template <int DT, int D>
 hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
-                         void* V_out, hipStream_t s) {
+                         void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s) {
     const dim3 grid((Bp + kGatherRows - 1) / kGatherRows, H);
-    hipLaunchKernelGGL((gather_rows_kernel<DT, D>), grid, dim3(kThreads), 0, s, idx, L, Bp, K, V, K_out, V_out);
+    hipLaunchKernelGGL((gather_rows_kernel<DT, D>), grid, dim3(kThreads), 0, s, idx, L, Bp, K, V, K_out, V_out, pos,
+                       pos_out);
     return hipGetLastError();
 }
 
@@ -420,12 +425,12 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
 }
 
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
-                         void* K_out, void* V_out, hipStream_t s) {
+                         void* K_out, void* V_out, hipStream_t s, const int32_t* pos, int32_t* pos_out) {
     if (dt == kBF16)
-        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, s)
-                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, s);
-    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, s)
-                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, s);
+        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s)
+                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s);
+    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s)
+                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s);
 }
 
 }  // namespace fc

@@ -118,3 +118,52 @@ def test_chunk_workspace_and_errors(fc):
     st = lib.fc_chunk_rel_l1_decide(ctypes.byref(p), arr, ctypes.c_void_p(4100), dummy, dummy, dummy, dummy, None,
                                     dummy, n, None)
     assert st == fc.FC_ERR_INVALID_ARG
+
+
+def _cache_params(fc, **kw):
+    base = dict(H=24, d=128, B_budget=7200, B_active=3600, lambda_=0.5, pool_window=7, softmax_scale=0.0,
+                dtype=fc.FC_BF16)
+    base.update(kw)
+    return fc.fc_cache_params(**base)
+
+
+def test_cache_workspace_query(fc):
+    c = _cache_params(fc)
+    n = fc.fc_cache_commit_workspace_bytes(c, 3600)
+    # the merged set (K, V rows and positions of B_total tokens) plus a
+    # compression of the largest merged set
+    merged = 2 * 24 * 10800 * 128 * 2 + 24 * 10800 * 4
+    kp = fc.fc_kv_params(24, 128, 3600, 10800, 7200, 0.5, 7, 0.0, fc.FC_BF16)
+    assert n >= merged + fc.fc_kv_compress_workspace_bytes(kp)
+    assert n % 256 == 0
+    for bad in (dict(H=0), dict(B_budget=0), dict(B_active=0), dict(lambda_=-0.1), dict(pool_window=2),
+                dict(d=80), dict(dtype=5), dict(B_budget=2 ** 31 - 10, B_active=100)):
+        assert fc.fc_cache_commit_workspace_bytes(_cache_params(fc, **bad), 3600) == 0, bad
+    assert fc.fc_cache_commit_workspace_bytes(c, 0) == 0
+
+
+def test_cache_argument_errors(fc):
+    lib = fc._lib
+    c = _cache_params(fc)
+    dummy = ctypes.c_void_p(4096)
+    need = fc.fc_cache_commit_workspace_bytes(c, 3600)
+
+    def commit(L_clean, L_c, pos0=0, Q=dummy, ws_bytes=need, p=c, K_chunk=dummy):
+        n = ctypes.c_int32(L_clean)
+        st = lib.fc_cache_commit(ctypes.byref(p), ctypes.byref(n), K_chunk, dummy, L_c, pos0, Q, 3600, dummy,
+                                 dummy, dummy, dummy, ws_bytes, None)
+        return st, n.value
+
+    assert commit(-1, 100) == (fc.FC_ERR_INVALID_ARG, -1)
+    assert commit(7201, 100) == (fc.FC_ERR_INVALID_ARG, 7201)
+    assert commit(0, 0) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 3601) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 100, pos0=-5) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 100, pos0=2 ** 31 - 50) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 100, K_chunk=ctypes.c_void_p(4104)) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 100, p=_cache_params(fc, d=96)) == (fc.FC_ERR_UNSUPPORTED, 0)
+    # a commit that overflows the budget needs queries and the workspace
+    assert commit(7200, 100, Q=None) == (fc.FC_ERR_INVALID_ARG, 7200)
+    assert commit(7200, 100, ws_bytes=need // 2) == (fc.FC_ERR_WORKSPACE, 7200)
+    assert lib.fc_cache_commit(ctypes.byref(c), None, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, dummy, dummy,
+                               need, None) == fc.FC_ERR_INVALID_ARG
