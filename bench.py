@@ -10,6 +10,10 @@ already resident in HBM:
   * fc_chunk_rel_l1_decide on 16 concurrent chunks of 64x8x90x160 bf16
     latents (steady state, all chunks active at staggered local steps).
 
+Beside the step it times a MAGI-like run of the KV cache manager
+(fc_cache_commit: chunks of 3600 tokens into a budget of 7200 per head) and
+reports it under "cache".
+
 Prints one JSON line.  `value` is clean-KV token-heads scored and selected per
 second over whole steps (the chunk decision included).  The dominant kernel
 (importance pass 1) is timed on its own with HIP events on the stream it runs
@@ -111,6 +115,49 @@ def cpu_baseline(cfg, ccfg, min_seconds: float):
                       f"decision of {ccfg.n_chunks} chunks (numpy)"}
 
 
+def cache_run(fc, synth, dev, reps: int):
+    """The MAGI-like cache run: chunks of 3600 tokens commit into a cache of
+    7200 per head, each compression scored by 3600 queries.  The run goes
+    through once untimed, then again with every commit timed on the stream
+    (HIP events); the compressing commits (third chunk on) are averaged.  The
+    append-only commit (copy of one chunk behind the clean rows) is timed on
+    its own for the copy kernel's bandwidth."""
+    import torch
+    cfg = synth.CACHE_CONFIGS["magi"]
+    log(f"generating the cache run: {cfg.n_chunks} chunks of {cfg.tokens_per_chunk} tokens, {cfg.H} heads")
+    Q, K, V = synth.cache_inputs(cfg, seed=0)
+    Q, K, V = Q.to(dev), K.to(dev), V.to(dev)
+    T = cfg.tokens_per_chunk
+    chunks = [(K[:, c * T:(c + 1) * T].contiguous(), V[:, c * T:(c + 1) * T].contiguous()) for c in range(cfg.n_chunks)]
+    del K, V
+    kv = fc.KvCache(cfg.H, cfg.d, cfg.B_budget, cfg.B_active, cfg.Lq, cfg.lam, cfg.w, torch.bfloat16, device=dev)
+    for _ in range(2):  # untimed pass, then the timed one (events only; the host runs ahead)
+        kv.length, kv.next_pos = 0, 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.n_chunks + 1)]
+        ev[0].record()
+        for c, (Kc, Vc) in enumerate(chunks):
+            kv.commit(Kc, Vc, Q[c])
+            ev[c + 1].record()
+        torch.cuda.synchronize()
+    times = [ev[c].elapsed_time(ev[c + 1]) for c in range(cfg.n_chunks)]
+    comp = [t for c, t in enumerate(times) if (c + 1) * T > cfg.B_budget]
+    merged = cfg.B_budget + T
+    commit_ms = statistics.mean(comp)
+    Kc, Vc = chunks[0]
+
+    def append():
+        fc.fc_cache_commit(kv.p, 0, Kc, Vc, 0, None, kv.K, kv.V, kv.pos, kv.workspace)
+    t_app = time_events(append, reps)
+    app_bytes = 2 * 2 * cfg.H * T * cfg.d * 2 + cfg.H * T * 4      # K and V rows read + written, positions
+    return {
+        "workload": f"MAGI-like cache run: {cfg.H} heads, d={cfg.d}, {cfg.n_chunks} chunks of {T} tokens, "
+                    f"budget {cfg.B_budget}, {cfg.Lq} queries per compression, lambda {cfg.lam}, bf16",
+        "compressing_commits": len(comp), "commit_ms": commit_ms, "commit_ms_max": max(comp),
+        "merged_token_heads_per_s": cfg.H * merged / (commit_ms * 1e-3),
+        "append_commit_ms": t_app, "append_gbps": app_bytes / (t_app * 1e-3) / 1e9,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +167,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time of the CPU-baseline (oracle) leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache", action="store_true", help="skip the KV-cache run")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
     args = ap.parse_args()
@@ -223,6 +271,12 @@ def main() -> int:
     for k, v in stages.items():
         log(f"  {k}: {v}")
 
+    cache = None
+    if not args.no_cache:
+        cache = cache_run(fc, synth, dev, reps)
+        for k, v in cache.items():
+            log(f"  cache {k}: {v}")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
@@ -257,6 +311,8 @@ def main() -> int:
         },
         "stages": stages,
     }
+    if cache is not None:
+        result["cache"] = cache
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on whole steps")
         result["cpu_baseline"] = cpu_baseline(cfg, ccfg, args.cpu_seconds)
