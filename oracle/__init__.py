@@ -310,3 +310,28 @@ def cache_commit(K_clean, V_clean, pos_clean, K_chunk, V_chunk, pos0: int, Q, B_
     idx = comp["idx"]
     pos = np.stack([pm[h][idx[h]] for h in range(pm.shape[0])])
     return {"K": comp["K_out"], "V": comp["V_out"], "pos": pos, "comp": comp, "merged": (Km, Vm, pm)}
+
+
+# ---------------------------------------------------------------------------
+# The sampler's Euler step with the decision fused (Key designs, item 1: the
+# L1 numerator is ||v dt||_1, the update itself)
+# ---------------------------------------------------------------------------
+
+def euler_step(x_t, v, offsets: Sequence[int], dt: Sequence[float], active: Sequence[bool]):
+    """X_{t-1} = X_t + v * dt_i over each active chunk i; inactive chunks keep
+    X_t's values.  The stored state is a rounded value, so this follows the
+    kernel's precision: the product and the sum each rounded to float32 (no
+    fused multiply-add), then the result rounded to the storage type of x_t
+    (bf16: to nearest, ties to even).  x_t, v: torch CPU tensors, flat."""
+    import torch
+    x32 = x_t.to(torch.float32).numpy()
+    v32 = v.to(torch.float32).numpy()
+    y = x32.copy()
+    for i in range(len(offsets) - 1):
+        if not active[i]:
+            continue
+        s, e = offsets[i], offsets[i + 1]
+        p = v32[s:e] * np.float32(dt[i])          # float32 product, rounded
+        y[s:e] = x32[s:e] + p                     # float32 sum, rounded
+    out = torch.from_numpy(y)
+    return out.to(x_t.dtype)

@@ -106,3 +106,79 @@ def test_resume_from_checkpoint():
         for n in range(n0, 50):
             r, f = oracle.decide(n, f, l1[n], 5, 0.01); rec.append(int(r))
         assert rec == full
+
+
+# --------------------------------------------------------------- Euler step (item 1: numerator = ||v dt||_1)
+
+def _bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def test_euler_exact_arithmetic_and_l1_closed_form():
+    # small integers and a power-of-two step: every value is exact, so the
+    # update is x + v dt and the L1 numerator is |dt| * sum |v| exactly
+    import torch
+    rng = np.random.default_rng(0)
+    x = rng.integers(-50, 50, size=300).astype(np.float32)
+    v = rng.integers(-20, 20, size=300).astype(np.float32)
+    offs, dts = [0, 100, 220, 300], [0.5, -0.25, 2.0]
+    for dtype in (torch.float32, torch.bfloat16):
+        xt, vt = torch.from_numpy(x).to(dtype), torch.from_numpy(v).to(dtype)
+        y = oracle.euler_step(xt, vt, offs, dts, [True, True, True])
+        for i in range(3):
+            s, e = offs[i], offs[i + 1]
+            want = x[s:e].astype(np.float64) + v[s:e].astype(np.float64) * dts[i]
+            assert (y[s:e].double().numpy() == want).all()
+        A, N = oracle.chunk_l1_sums(xt, y, offs)
+        for i in range(3):
+            s, e = offs[i], offs[i + 1]
+            assert A[i] == abs(dts[i]) * np.abs(v[s:e]).sum()
+            assert N[i] == np.abs(x[s:e]).sum()
+
+
+def test_euler_storage_rounding_ties_to_even():
+    # bf16 has 8 significant bits: near 1 its spacing is 2^-7, so adding 2^-8
+    # lands exactly half-way and rounds to the even neighbour
+    import torch
+    x = torch.tensor([1.0, 1.0 + 2.0 ** -7, -1.0, 3.0], dtype=torch.bfloat16)
+    v = torch.tensor([1.0, 1.0, -1.0, 0.0], dtype=torch.bfloat16)
+    y = oracle.euler_step(x, v, [0, 4], [2.0 ** -8], [True])
+    assert y.tolist() == [1.0, 1.0 + 2.0 ** -6, -1.0, 3.0]
+
+
+def test_euler_product_and_sum_rounded_separately():
+    # with a fused multiply-add the result would be 2^-46; rounding the
+    # product to float32 first cancels it to exactly 0
+    import torch
+    a = 1.0 + 2.0 ** -23
+    x = torch.tensor([-(1.0 + 2.0 ** -22)], dtype=torch.float32)
+    v = torch.tensor([a], dtype=torch.float32)
+    y = oracle.euler_step(x, v, [0, 1], [a], [True])
+    assert y.item() == 0.0
+    exact = float(x.item()) + a * a
+    assert exact == 2.0 ** -46
+
+
+def test_euler_inactive_chunks_keep_their_values():
+    import torch
+    x = torch.arange(10, dtype=torch.float32)
+    v = torch.ones(10, dtype=torch.float32)
+    y = oracle.euler_step(x, v, [0, 4, 10], [1.0, 1.0], [False, True])
+    assert y[:4].tolist() == x[:4].tolist() and y[4:].tolist() == (x[4:] + 1).tolist()
+
+
+def test_euler_follows_the_synthetic_path():
+    # the synthetic trajectory is X_t = X_N - v (1 - sigma(t)); one Euler step
+    # of size sigma(t-1) - sigma(t) from X_t reaches X_{t-1} up to float32
+    # rounding of the two routes
+    cfg = synth.CHUNK_CONFIGS["tiny"]
+    tr = synth.ChunkTrajectory(cfg, seed=0)
+    import torch
+    for t in (10, 5, 1):
+        xt = torch.from_numpy(np.concatenate([tr.state_f32(i, t) for i in range(cfg.n_chunks)]))
+        want = np.concatenate([tr.state_f32(i, t - 1) for i in range(cfg.n_chunks)])
+        v = torch.from_numpy(tr.v.reshape(-1).copy())
+        dts = [tr.sigma(t - 1) - tr.sigma(t)] * cfg.n_chunks
+        # X_{t-1} - X_t = v (sigma(t-1) - sigma(t)): velocity v, step sigma(t-1) - sigma(t) < 0
+        y = oracle.euler_step(xt, v, tr.offsets, dts, [True] * cfg.n_chunks).numpy()
+        assert np.max(np.abs(y - want)) <= 4 * np.finfo(np.float32).eps * (np.abs(want).max() + 1)
