@@ -281,6 +281,29 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
                                  int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fc_euler_step_l1_decide -- the sampler's Euler step with the decision fused.
+ * Item 1 writes the L1 numerator as ||v dt||_1: the update X_{t-1} = X_t + v dt
+ * itself.  For every active chunk i:
+ *   X_next = X_t + v * dt[i]   per element, in float32 (the product and the sum
+ *                              each rounded, no fused multiply-add), then
+ *                              rounded to the storage type (bf16: to nearest,
+ *                              ties to even);
+ * then the decision exactly as fc_chunk_rel_l1_decide on (X_t, X_next): the
+ * same sums in the same order, so the same bits.
+ *   v       device, dtype: the velocity, laid out as the states
+ *   dt      device f32[n_chunks]: each chunk's step of the schedule
+ *   X_next  device, dtype: the next state; may be X_t itself (in-place
+ *           update), otherwise it must not overlap X_t or v
+ * Inactive chunks (step < 0) are neither read nor written.  Other arguments,
+ * the workspace and errors as for fc_chunk_rel_l1_decide (same workspace
+ * query).
+ */
+fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets,
+                                  const void* X_t, const void* v, const float* dt, void* X_next,
+                                  int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

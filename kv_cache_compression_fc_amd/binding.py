@@ -34,7 +34,7 @@ EXPORTS = (
     "fc_kv_importance_lse", "fc_kv_importance_colsum",
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
     "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
-    "fc_cache_commit_workspace_bytes", "fc_cache_commit",
+    "fc_cache_commit_workspace_bytes", "fc_cache_commit", "fc_euler_step_l1_decide",
 )
 
 
@@ -89,6 +89,8 @@ _lib.fc_cache_commit_workspace_bytes.argtypes = [ctypes.POINTER(fc_cache_params)
 _lib.fc_cache_commit.restype = ctypes.c_int
 _lib.fc_cache_commit.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.POINTER(ctypes.c_int32), _vp, _vp,
                                  ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_euler_step_l1_decide.restype = ctypes.c_int
+_lib.fc_euler_step_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p] + [_vp] * 8 + [_vp, _sz, _vp]
 
 
 class FlowCacheError(RuntimeError):
@@ -284,6 +286,12 @@ class ChunkDecider:
         fc_chunk_rel_l1_decide(self.p, self.offsets, X_t, X_tm1, self.step, self.f, self.recompute, self.l1,
                                self.workspace, stream)
 
+    def euler_step(self, X_t: torch.Tensor, v: torch.Tensor, dt: torch.Tensor, X_next: torch.Tensor,
+                   stream=None) -> None:
+        """X_next = X_t + v dt per chunk (dt: device f32 [n_chunks]) and the decision on that pair."""
+        fc_euler_step_l1_decide(self.p, self.offsets, X_t, v, dt, X_next, self.step, self.f, self.recompute, self.l1,
+                                self.workspace, stream)
+
 
 def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, step, f, recompute,
                            l1_rel_out=None, workspace=None, stream=None) -> None:
@@ -333,3 +341,10 @@ class KvCache:
                                       self.pos, self.workspace, stream)
         self.next_pos += int(K_chunk.shape[1])
         return self.length
+
+
+def fc_euler_step_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, v, dt, X_next, step, f, recompute,
+                            l1_rel_out=None, workspace=None, stream=None) -> None:
+    _check("fc_euler_step_l1_decide", _lib.fc_euler_step_l1_decide(
+        ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(v), _ptr(dt), _ptr(X_next), _ptr(step), _ptr(f),
+        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))

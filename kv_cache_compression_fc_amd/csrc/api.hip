@@ -403,4 +403,20 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
                                       static_cast<hipStream_t>(stream)));
 }
 
+fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,
+                                  const void* v, const float* dt, void* X_next, int32_t* step, float* f,
+                                  uint8_t* recompute, float* l1_rel_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    ChunkTable tab;
+    fc_status st = chunk_table(p, chunk_offsets, &tab);
+    if (st != FC_OK) return st;
+    if (!X_t || !v || !dt || !X_next || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
+    if (!aligned16(X_t) || !aligned16(v) || !aligned16(X_next)) return FC_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    const int dtp = p->dtype == FC_BF16 ? kBF16 : kF32;
+    return hip_status(launch_chunk_l1(dtp, tab, X_t, v, step, f, recompute, l1_rel_out,
+                                      static_cast<float2*>(workspace), p->m, p->eps,
+                                      static_cast<hipStream_t>(stream), dt, X_next));
+}
+
 }  // extern "C"

@@ -13,6 +13,14 @@
 // device.  The kernel boundary orders the two (no cross-XCD fences or
 // atomics), and the result is deterministic.  HBM-bound: every state byte is
 // read once, with non-temporal loads.
+//
+// Fused variant: item 1 writes the numerator as ||v dt||_1, the sampler's own
+// update, so the slab kernel can take X_t and the velocity v instead of two
+// states, write the Euler update X_{t-1} = X_t + v dt_i itself and sum
+// |X_{t-1} - X_t| from the value it stores: three streams instead of the five
+// of an update kernel followed by the L1 pass.  The slabs and the order of
+// every sum are those of the unfused kernel, so the decision is the one
+// fc_chunk_rel_l1_decide takes on (X_t, the stored X_{t-1}), bit for bit.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,17 +58,84 @@ __device__ __forceinline__ void accum16<kF32>(const uint4& a, const uint4& b, fl
     }
 }
 
+// Storage rounding of a float32 value: bf16 to nearest, ties to even
+// (finite inputs); float32 unchanged.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float y) {
+    const uint32_t u = __float_as_uint(y);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Euler update of one element in float32: the product and the sum are each
+// rounded (no fused multiply-add), then the result is rounded to storage.
+__device__ __forceinline__ float euler_f32(float x, float v, float dt) {
+#pragma clang fp contract(off)
+    const float p = v * dt;
+    return x + p;
+}
+
+template <int DT>
+__device__ __forceinline__ void euler16(const uint4& a, const uint4& b, float dt, uint4& out, float& sa, float& sn);
+template <>
+__device__ __forceinline__ void euler16<kBF16>(const uint4& a, const uint4& b, float dt, uint4& out, float& sa,
+                                               float& sn) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    uint32_t wy[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a0 = __uint_as_float(wa[i] << 16), a1 = __uint_as_float(wa[i] & 0xffff0000u);
+        const float v0 = __uint_as_float(wb[i] << 16), v1 = __uint_as_float(wb[i] & 0xffff0000u);
+        const uint32_t y0 = bf16_rne_bits(euler_f32(a0, v0, dt)), y1 = bf16_rne_bits(euler_f32(a1, v1, dt));
+        wy[i] = y0 | (y1 << 16);
+        const float b0 = __uint_as_float(y0 << 16), b1 = __uint_as_float(y1 << 16);
+        sa += fabsf(b0 - a0) + fabsf(b1 - a1);
+        sn += fabsf(a0) + fabsf(a1);
+    }
+    out = make_uint4(wy[0], wy[1], wy[2], wy[3]);
+}
+template <>
+__device__ __forceinline__ void euler16<kF32>(const uint4& a, const uint4& b, float dt, uint4& out, float& sa,
+                                              float& sn) {
+    const float fa[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
+    const float fv[4] = {__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
+    float fy[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fy[i] = euler_f32(fa[i], fv[i], dt);
+        sa += fabsf(fy[i] - fa[i]);
+        sn += fabsf(fa[i]);
+    }
+    out = make_uint4(__float_as_uint(fy[0]), __float_as_uint(fy[1]), __float_as_uint(fy[2]), __float_as_uint(fy[3]));
+}
+
+template <int DT>
+__device__ __forceinline__ float euler_scalar(void* y_out, long long i, float x, float v, float dt) {
+    const float y = euler_f32(x, v, dt);
+    if constexpr (DT == kBF16) {
+        const uint32_t b = bf16_rne_bits(y);
+        static_cast<uint16_t*>(y_out)[i] = (uint16_t)b;
+        return __uint_as_float(b << 16);
+    } else {
+        static_cast<float*>(y_out)[i] = y;
+        return y;
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ float load_scalar(const void* p, long long i) {
     if constexpr (DT == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
     else return static_cast<const float*>(p)[i];
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable tab, const void* __restrict__ X_t,
+// One slab per workgroup.  EULER = false: the second input is X_{t-1}.
+// EULER = true: the second input is the velocity v; the kernel writes
+// X_{t-1} = X_t + v dt[c] to X_next (which may be X_t itself: every element
+// is read before it is written, by the same lane) and sums against it.
+template <int DT, bool EULER>
+__global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable tab, const void* X_t,
                                                                     const void* __restrict__ X_tm1,
                                                                     const int32_t* __restrict__ step,
-                                                                    float2* __restrict__ partial) {
+                                                                    float2* __restrict__ partial,
+                                                                    const float* __restrict__ dt, void* X_next) {
     constexpr int V = vec_elems<DT>();
     constexpr long long EPB = slab_elems<DT>();
     __shared__ float red_a[kThreads / kWave], red_n[kThreads / kWave];
@@ -73,6 +148,7 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable t
     }
     const int c = lo;
     if (step[c] < 0) return;  // inactive chunk: nothing is read or written
+    const float h = EULER ? dt[c] : 0.f;
 
     const long long s0 = tab.off[c] + (long long)(bid - tab.blk_start[c]) * EPB;
     const long long e0 = min(s0 + EPB, tab.off[c + 1]);
@@ -81,15 +157,20 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable t
     float sa = 0.f, sn = 0.f;
     // unaligned head and tail (fewer than V elements each)
     if (threadIdx.x < a0 - s0) {
-        const float x = load_scalar<DT>(X_t, s0 + threadIdx.x), y = load_scalar<DT>(X_tm1, s0 + threadIdx.x);
+        const long long i = s0 + threadIdx.x;
+        const float x = load_scalar<DT>(X_t, i), b = load_scalar<DT>(X_tm1, i);
+        const float y = EULER ? euler_scalar<DT>(X_next, i, x, b, h) : b;
         sa += fabsf(y - x); sn += fabsf(x);
     }
     if (threadIdx.x < e0 - a1) {
-        const float x = load_scalar<DT>(X_t, a1 + threadIdx.x), y = load_scalar<DT>(X_tm1, a1 + threadIdx.x);
+        const long long i = a1 + threadIdx.x;
+        const float x = load_scalar<DT>(X_t, i), b = load_scalar<DT>(X_tm1, i);
+        const float y = EULER ? euler_scalar<DT>(X_next, i, x, b, h) : b;
         sa += fabsf(y - x); sn += fabsf(x);
     }
     const uint4* va = reinterpret_cast<const uint4*>(X_t) + a0 / V;
     const uint4* vb = reinterpret_cast<const uint4*>(X_tm1) + a0 / V;
+    uint4* vy = EULER ? reinterpret_cast<uint4*>(X_next) + a0 / V : nullptr;
     const int nvec = (int)((a1 - a0) / V);
     int v = threadIdx.x;
     for (; v + (kUnroll - 1) * kThreads < nvec; v += kUnroll * kThreads) {
@@ -100,9 +181,25 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable t
             xb[u] = load_stream16(vb + v + u * kThreads);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) accum16<DT>(xa[u], xb[u], sa, sn);
+        for (int u = 0; u < kUnroll; ++u) {
+            if constexpr (EULER) {
+                uint4 y;
+                euler16<DT>(xa[u], xb[u], h, y, sa, sn);
+                store_stream16(vy + v + u * kThreads, y);
+            } else {
+                accum16<DT>(xa[u], xb[u], sa, sn);
+            }
+        }
     }
-    for (; v < nvec; v += kThreads) accum16<DT>(va[v], vb[v], sa, sn);
+    for (; v < nvec; v += kThreads) {
+        if constexpr (EULER) {
+            uint4 y;
+            euler16<DT>(va[v], vb[v], h, y, sa, sn);
+            vy[v] = y;
+        } else {
+            accum16<DT>(va[v], vb[v], sa, sn);
+        }
+    }
 
     sa = wave_sum(sa);
     sn = wave_sum(sn);
@@ -159,10 +256,15 @@ __global__ __launch_bounds__(kThreads) void chunk_decide_kernel(ChunkTable tab, 
 
 template <int DT>
 hipError_t l1_launch(const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step, float* f,
-                     uint8_t* recompute, float* l1_out, float2* partial, int m, float eps, hipStream_t s) {
+                     uint8_t* recompute, float* l1_out, float2* partial, int m, float eps, hipStream_t s,
+                     const float* dt, void* X_next) {
     const int blocks = tab.blk_start[tab.n];
-    hipLaunchKernelGGL(chunk_l1_partial_kernel<DT>, dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1, step,
-                       partial);
+    if (X_next != nullptr)
+        hipLaunchKernelGGL((chunk_l1_partial_kernel<DT, true>), dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1,
+                           step, partial, dt, X_next);
+    else
+        hipLaunchKernelGGL((chunk_l1_partial_kernel<DT, false>), dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1,
+                           step, partial, nullptr, nullptr);
     hipLaunchKernelGGL(chunk_decide_kernel, dim3(tab.n), dim3(kThreads), 0, s, tab, partial, step, f, recompute,
                        l1_out, m, eps);
     return hipGetLastError();
@@ -178,9 +280,10 @@ int chunk_blocks_for(long long elems, int dt) {
 
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step,
                            float* f, uint8_t* recompute, float* l1_out, float2* partial, int m, float eps,
-                           hipStream_t s) {
-    if (dt == kBF16) return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s);
-    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s);
+                           hipStream_t s, const float* step_dt, void* X_next) {
+    if (dt == kBF16)
+        return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next);
+    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next);
 }
 
 }  // namespace fc

@@ -92,8 +92,12 @@ struct ChunkTable {
     long long off[kMaxChunks + 1];
 };
 int chunk_blocks_for(long long elems, int dt);
+// With X_next != nullptr, X_tm1 is the velocity v instead: the slab kernel
+// writes X_next = X_t + v * step_dt[chunk] (Euler update, rounded to the
+// storage type) and measures the L1 against it.
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1,
                            int32_t* step, float* f, uint8_t* recompute, float* l1_out, float2* partial,
-                           int m, float eps, hipStream_t s);
+                           int m, float eps, hipStream_t s, const float* step_dt = nullptr,
+                           void* X_next = nullptr);
 
 }  // namespace fc

@@ -217,6 +217,20 @@ class ChunkTrajectory:
     def state(self, i: int, t: int) -> torch.Tensor:
         return _to_storage(self.state_f32(i, t), self.cfg.dtype)
 
+    def velocity(self) -> torch.Tensor:
+        """The path's velocity, flat over the chunks, in the storage dtype:
+        X_{t-1} - X_t = v (sigma(t-1) - sigma(t))."""
+        return _to_storage(self.v.reshape(-1), self.cfg.dtype)
+
+    def step_size(self, n: int) -> float:
+        """sigma(t-1) - sigma(t) at local step n (t = N - n): the Euler step."""
+        t = self.cfg.N - n
+        return self.sigma(t - 1) - self.sigma(t)
+
+    def noise_states(self) -> torch.Tensor:
+        """X_N of every chunk, flat, in the storage dtype."""
+        return _to_storage(self.x_noise.reshape(-1), self.cfg.dtype)
+
     def n_global_steps(self) -> int:
         return self.cfg.N + (self.cfg.n_chunks - 1) * self.cfg.start_stride
 

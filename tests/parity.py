@@ -14,8 +14,12 @@ fp64 oracle on identical input values):
 import numpy as np
 import torch
 
+import oracle
+
 REL = 1e-3
 BAND = 1e-4
+L1_RTOL = 1e-5       # float32 slab sums vs fp64 (reported value only)
+EPS_BAND = 1e-6      # decisions within this distance of eps are exempt
 
 
 def max_rel_err(got, want):
@@ -94,3 +98,32 @@ def check_selection_consistent(idx_gpu, score_gpu, B):
             kt = np.nonzero(keep & (sc[h] == kmin))[0]
             dt = np.nonzero(~keep & (sc[h] == kmin))[0]
             assert kt.max() < dt.min()
+
+
+class DecisionLockstep:
+    """Oracle state per chunk, advanced beside the GPU's."""
+
+    def __init__(self, n, m, eps):
+        self.f = np.zeros(n)
+        self.m, self.eps = m, eps
+        self.exempt = 0
+        self.decisions = 0
+
+    def step(self, steps, l1_ref, rec_gpu, f_gpu, l1_gpu):
+        for i, n in enumerate(steps):
+            if n < 0:
+                continue
+            f_prev = self.f[i]
+            r, f_new = oracle.decide(n, f_prev, l1_ref[i], self.m, self.eps)
+            if np.isfinite(l1_ref[i]):
+                assert abs(l1_gpu[i] - l1_ref[i]) <= L1_RTOL * l1_ref[i] + 1e-12, (i, n, l1_gpu[i], l1_ref[i])
+            else:
+                assert l1_gpu[i] == np.inf
+            exempt = n >= self.m and abs(f_prev + l1_ref[i] - self.eps) <= EPS_BAND
+            self.decisions += 1
+            if exempt:
+                self.exempt += 1
+            else:
+                assert bool(rec_gpu[i]) == r, f"chunk {i} local step {n}: gpu {rec_gpu[i]} oracle {r}"
+                assert abs(f_gpu[i] - f_new) <= 1e-6, (i, n, f_gpu[i], f_new)
+            self.f[i] = f_new if bool(rec_gpu[i]) == r else float(f_gpu[i])
