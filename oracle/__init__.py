@@ -335,3 +335,35 @@ def euler_step(x_t, v, offsets: Sequence[int], dt: Sequence[float], active: Sequ
         y[s:e] = x32[s:e] + p                     # float32 sum, rounded
     out = torch.from_numpy(y)
     return out.to(x_t.dtype)
+
+
+# ---------------------------------------------------------------------------
+# Other decision policies over the same relative L1
+# ---------------------------------------------------------------------------
+
+def uniform_l1_rel(x_t, x_tm1, offsets: Sequence[int], active: Sequence[bool]) -> float:
+    """One relative L1 over every active chunk: the sum of the chunks'
+    ||X_{t-1} - X_t||_1 over the sum of their ||X_t||_1 (+inf when that sum
+    is 0).  The uniform policy the FlowCache page contrasts with
+    (背景与动机: one decision for all content at a timestep)."""
+    A, N = chunk_l1_sums(x_t, x_tm1, offsets)
+    a = float(sum(A[i] for i in range(len(A)) if active[i]))
+    n = float(sum(N[i] for i in range(len(N)) if active[i]))
+    return a / n if n > 0 else math.inf
+
+
+def decide_history(n: int, acc: float, dev: float, m: int, delta: float) -> Tuple[bool, float]:
+    """ARCache's History-Guided Cache ("Accelerating Autoregressive Video
+    Diffusion via History-Guided Cache and Residual Correction", papernotes
+    digest, Key designs item 1): the cache is reused while the deviations
+    summed from the last refresh step t_ref, that step included, through the
+    current one stay <= delta; otherwise it refreshes and t_ref becomes the
+    current step.  acc holds the sum through the previous step; returns
+    (refresh, the sum through this step from the new t_ref).  The first m
+    steps refresh."""
+    if n < m:
+        return True, dev
+    a = acc + dev
+    if a > delta:
+        return True, dev
+    return False, a

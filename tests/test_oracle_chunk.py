@@ -182,3 +182,52 @@ def test_euler_follows_the_synthetic_path():
         # X_{t-1} - X_t = v (sigma(t-1) - sigma(t)): velocity v, step sigma(t-1) - sigma(t) < 0
         y = oracle.euler_step(xt, v, tr.offsets, dts, [True] * cfg.n_chunks).numpy()
         assert np.max(np.abs(y - want)) <= 4 * np.finfo(np.float32).eps * (np.abs(want).max() + 1)
+
+
+# --------------------------------------------------------------- other policies
+
+def test_history_rule_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "history_hand_example.json")))
+    acc, f, ref, rec = 0.0, 0.0, [], []
+    sums, fs = [], []
+    for n, dv in enumerate(g["deviation"]):
+        r, acc = oracle.decide_history(n, acc, dv, g["m"], g["delta"])
+        ref.append(int(r)); sums.append(acc)
+        r2, f = oracle.decide(n, f, dv, g["m"], g["delta"])
+        rec.append(int(r2)); fs.append(f)
+    assert ref == g["expect_history_refresh"] and sums == g["expect_history_sum"]
+    assert rec == g["expect_flowcache_recompute"] and fs == g["expect_flowcache_f"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_history_rule_matches_the_window_sum(seed):
+    # the page's condition, evaluated from scratch at every step: refresh at t
+    # iff the deviations from the last refresh step through t sum past delta
+    rng = np.random.default_rng(seed)
+    devs = rng.exponential(0.05, size=200)
+    delta, m = 0.12, 3
+    acc, refreshes, t_ref = 0.0, [], None
+    for n, dv in enumerate(devs):
+        r, acc = oracle.decide_history(n, acc, dv, m, delta)
+        if n < m:
+            want = True
+        else:
+            window = devs[t_ref:n + 1]          # t_ref .. current step, both included
+            want = float(np.sum(window)) > delta
+        assert r == want, n
+        if r:
+            t_ref = n
+        refreshes.append(r)
+    assert 10 < sum(refreshes) < 150
+
+
+def test_uniform_l1_is_the_ratio_of_sums():
+    import torch
+    x = torch.tensor([1.0, -2.0, 3.0, 4.0, 0.5, -0.5], dtype=torch.float64)
+    y = torch.tensor([1.5, -2.0, 2.0, 4.0, 1.5, -0.5], dtype=torch.float64)
+    offs = [0, 2, 4, 6]
+    # chunk sums: A = (0.5, 1.0, 1.0), N = (3, 7, 1)
+    assert oracle.uniform_l1_rel(x, y, offs, [True, True, True]) == 2.5 / 11
+    assert oracle.uniform_l1_rel(x, y, offs, [True, False, True]) == 1.5 / 4
+    assert oracle.uniform_l1_rel(x, y, offs, [False, True, False]) == oracle.chunk_l1_rel(x, y, offs)[1]
+    assert oracle.uniform_l1_rel(x * 0, y, offs, [True, True, True]) == math.inf
