@@ -253,12 +253,23 @@ def main() -> int:
     t_compress = time_events(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws),
                              reps)
     t_l1 = time_events(lambda: dec.decide(xt_d, xtm1_d), reps)
+    # the fused variant: Euler update X_{t-1} = X_t + v dt and the decision in
+    # one pass, in place, on the same 16 chunks (velocity: the path's own)
+    v_d = synth.ChunkTrajectory(ccfg, seed=0).velocity().to(dev)
+    x_work = xt_d.clone()
+    dts = torch.full((ccfg.n_chunks,), -1e-4, dtype=torch.float32, device=dev)
+    dec_fused = fc.ChunkDecider([i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)], ccfg.m, ccfg.eps[0],
+                                torch.bfloat16, dev)
+    dec_fused.step.copy_(torch.tensor(steps, dtype=torch.int32))   # every chunk active; the counters advance
+    t_fused = time_events(lambda: dec_fused.euler_step(x_work, v_d, dts, x_work), reps)
+    del v_d, x_work
     torch.cuda.synchronize()
 
     mfma_flops = 2.0 * H * Lq * Lk * d            # one Q K^T product (each pass executes one)
     red_bytes = H * Lk * (d * 2 + 4)              # read K once, write r
     sel_bytes = 8 * H * Lk + 4 * H * Bp + 2 * 2 * H * Bp * d * 2   # imp + r, idx, K/V rows read + written
     l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
+    fused_bytes = 3 * ccfg.n_chunks * ccfg.chunk_elems * 2          # X_t and v read, X_{t-1} written
     lse_tflops = mfma_flops / (t_lse * 1e-3) / 1e12
     stages = {
         "importance_lse_ms": t_lse, "importance_lse_tflops": lse_tflops,
@@ -266,6 +277,7 @@ def main() -> int:
         "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
+        "euler_l1_fused_ms": t_fused, "euler_l1_fused_gbps": fused_bytes / (t_fused * 1e-3) / 1e9,
         "timing": f"events; redundancy {how_red}, select {how_sel}",
     }
     for k, v in stages.items():

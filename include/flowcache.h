@@ -304,6 +304,49 @@ fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_of
                                   int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fc_uniform_rel_l1_decide -- the uniform policy the FlowCache page contrasts
+ * with (背景与动机: TeaCache-style caches take one reuse/recompute decision
+ * for all content at a timestep): one relative L1 over every active chunk,
+ *   L1_rel = sum_i ||X^i_{t-1} - X^i_t||_1 / sum_i ||X^i_t||_1  (active i),
+ * one accumulator f and one step counter, the rule of item 2, and the same
+ * decision for every active chunk.
+ *   chunk_step  device int32[n_chunks], read only: < 0 marks an inactive
+ *               chunk (not read, its recompute flag untouched)
+ *   step        device int32[1] in/out: the shared local step
+ *   f           device f32[1] in/out
+ *   recompute   device uint8[n_chunks] out (active chunks only)
+ *   l1_rel_out  device f32[1], nullable
+ * Other arguments, the workspace query and errors as for
+ * fc_chunk_rel_l1_decide.
+ */
+fc_status fc_uniform_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets,
+                                   const void* X_t, const void* X_tm1, const int32_t* chunk_step,
+                                   int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_history_rel_l1_decide -- the History-Guided Cache rule of ARCache (page
+ * "Accelerating Autoregressive Video Diffusion via History-Guided Cache and
+ * Residual Correction", papernotes CVPR 2026 digest, 关键设计 item 1), per
+ * segment i of the history tokens:
+ *   Delta_i = ||h_t - h_{t+1}||_1 / ||h_{t+1}||_1
+ * (h_prev = h_{t+1}, the previous step's history tokens; h_cur = h_t).  The
+ * cache is reused while the deviations summed from the last refresh step
+ * t_ref (that step included) through this one stay <= delta (p->eps);
+ * otherwise it refreshes and t_ref becomes this step, so the sum restarts at
+ * this step's Delta:
+ *   n < m:  refresh = 1, acc = Delta;
+ *   else a = acc + Delta;  a > delta: refresh = 1, acc = Delta;  else refresh = 0, acc = a;
+ *   then step = n + 1.
+ * Arguments as for fc_chunk_rel_l1_decide (segments in place of chunks;
+ * dev_out, nullable, receives Delta; +inf when ||h_{t+1}||_1 = 0).
+ */
+fc_status fc_history_rel_l1_decide(const fc_l1_params* p, const int64_t* segment_offsets,
+                                   const void* h_prev, const void* h_cur,
+                                   int32_t* step, float* acc, uint8_t* refresh, float* dev_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,7 @@ EXPORTS = (
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
     "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
     "fc_cache_commit_workspace_bytes", "fc_cache_commit", "fc_euler_step_l1_decide",
+    "fc_uniform_rel_l1_decide", "fc_history_rel_l1_decide",
 )
 
 
@@ -91,6 +92,10 @@ _lib.fc_cache_commit.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.POINTER
                                  ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_euler_step_l1_decide.restype = ctypes.c_int
 _lib.fc_euler_step_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p] + [_vp] * 8 + [_vp, _sz, _vp]
+_lib.fc_uniform_rel_l1_decide.restype = ctypes.c_int
+_lib.fc_uniform_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p] + [_vp] * 7 + [_vp, _sz, _vp]
+_lib.fc_history_rel_l1_decide.restype = ctypes.c_int
+_lib.fc_history_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p] + [_vp] * 6 + [_vp, _sz, _vp]
 
 
 class FlowCacheError(RuntimeError):
@@ -348,3 +353,17 @@ def fc_euler_step_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, 
     _check("fc_euler_step_l1_decide", _lib.fc_euler_step_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(v), _ptr(dt), _ptr(X_next), _ptr(step), _ptr(f),
         _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def fc_uniform_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, chunk_step, step, f,
+                             recompute, l1_rel_out=None, workspace=None, stream=None) -> None:
+    _check("fc_uniform_rel_l1_decide", _lib.fc_uniform_rel_l1_decide(
+        ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(chunk_step), _ptr(step), _ptr(f),
+        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def fc_history_rel_l1_decide(p: fc_l1_params, segment_offsets: Sequence[int], h_prev, h_cur, step, acc, refresh,
+                             dev_out=None, workspace=None, stream=None) -> None:
+    _check("fc_history_rel_l1_decide", _lib.fc_history_rel_l1_decide(
+        ctypes.byref(p), _offsets(segment_offsets), _ptr(h_prev), _ptr(h_cur), _ptr(step), _ptr(acc), _ptr(refresh),
+        _ptr(dev_out), _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -419,4 +419,37 @@ fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_of
                                       static_cast<hipStream_t>(stream), dt, X_next));
 }
 
+fc_status fc_uniform_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,
+                                   const void* X_tm1, const int32_t* chunk_step, int32_t* step, float* f,
+                                   uint8_t* recompute, float* l1_rel_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    ChunkTable tab;
+    fc_status st = chunk_table(p, chunk_offsets, &tab);
+    if (st != FC_OK) return st;
+    if (!X_t || !X_tm1 || !chunk_step || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
+    if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, const_cast<int32_t*>(chunk_step), f, recompute,
+                                      l1_rel_out, static_cast<float2*>(workspace), p->m, p->eps,
+                                      static_cast<hipStream_t>(stream), nullptr, nullptr, kRuleUniform, step));
+}
+
+fc_status fc_history_rel_l1_decide(const fc_l1_params* p, const int64_t* segment_offsets, const void* h_prev,
+                                   const void* h_cur, int32_t* step, float* acc, uint8_t* refresh,
+                                   float* dev_out, void* workspace, size_t workspace_bytes, void* stream) {
+    ChunkTable tab;
+    fc_status st = chunk_table(p, segment_offsets, &tab);
+    if (st != FC_OK) return st;
+    if (!h_prev || !h_cur || !step || !acc || !refresh) return FC_ERR_INVALID_ARG;
+    if (!aligned16(h_prev) || !aligned16(h_cur)) return FC_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    // ||h_t - h_{t+1}||_1 / ||h_{t+1}||_1: the previous state takes the
+    // denominator's place, the first argument of the slab pass
+    return hip_status(launch_chunk_l1(dt, tab, h_prev, h_cur, step, acc, refresh, dev_out,
+                                      static_cast<float2*>(workspace), p->m, p->eps,
+                                      static_cast<hipStream_t>(stream), nullptr, nullptr, kRuleHistory));
+}
+
 }  // extern "C"

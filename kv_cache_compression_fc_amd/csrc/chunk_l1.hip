@@ -215,6 +215,13 @@ __global__ __launch_bounds__(kThreads) void chunk_l1_partial_kernel(ChunkTable t
 
 // One workgroup per chunk: L1_rel from the chunk's slab pairs, then the
 // reuse decision.
+//   kRuleChunkwise (FlowCache, Key designs item 2): a = f + L1_rel; recompute and
+//     reset f to 0 when a > eps (and on the first m steps), else f = a.
+//   kRuleHistory (ARCache, History-Guided Cache): the sum of the deviations since
+//     the last refresh step, that step included: a = f + L1_rel; a > eps
+//     refreshes and restarts the sum at this step's deviation (f = L1_rel),
+//     else f = a; the first m steps refresh (f = L1_rel).
+template <int RULE>
 __global__ __launch_bounds__(kThreads) void chunk_decide_kernel(ChunkTable tab, const float2* __restrict__ partial,
                                                                 int32_t* __restrict__ step, float* __restrict__ f,
                                                                 uint8_t* __restrict__ recompute,
@@ -238,14 +245,15 @@ __global__ __launch_bounds__(kThreads) void chunk_decide_kernel(ChunkTable tab, 
         double TA = 0.0, TN = 0.0;
         for (int w = 0; w < kThreads / kWave; ++w) { TA += fin_a[w]; TN += fin_n[w]; }
         const float l1 = TN > 0.0 ? (float)(TA / TN) : INFINITY;
+        const float f_reset = RULE == kRuleHistory ? l1 : 0.f;
         float f_new;
         uint8_t rec;
         if (n_step < m) {
-            rec = 1; f_new = 0.f;                   // forced recompute, f = 0
+            rec = 1; f_new = f_reset;                   // forced recompute
         } else {
             const float a = f[c] + l1;
-            if (a > eps) { rec = 1; f_new = 0.f; }  // recompute and reset
-            else { rec = 0; f_new = a; }            // reuse and accumulate
+            if (a > eps) { rec = 1; f_new = f_reset; }  // recompute, restart the sum
+            else { rec = 0; f_new = a; }                // reuse and accumulate
         }
         f[c] = f_new;
         recompute[c] = rec;
@@ -254,10 +262,59 @@ __global__ __launch_bounds__(kThreads) void chunk_decide_kernel(ChunkTable tab, 
     }
 }
 
+// Uniform policy: one L1_rel over every active chunk (sum of the numerators
+// over sum of the denominators, slab pairs added chunk by chunk in order),
+// one accumulator and step counter, the rule of Key designs item 2, and the
+// same decision written for every active chunk.  One workgroup.
+__global__ __launch_bounds__(kThreads) void uniform_decide_kernel(ChunkTable tab, const float2* __restrict__ partial,
+                                                                  const int32_t* __restrict__ chunk_step,
+                                                                  int32_t* __restrict__ step, float* __restrict__ f,
+                                                                  uint8_t* __restrict__ recompute,
+                                                                  float* __restrict__ l1_out, int m, float eps) {
+    __shared__ double fin_a[kThreads / kWave], fin_n[kThreads / kWave];
+    __shared__ uint8_t rec_s;
+    double A = 0.0, N = 0.0;
+    for (int c = 0; c < tab.n; ++c) {
+        if (chunk_step[c] < 0) continue;
+        for (int b = tab.blk_start[c] + threadIdx.x; b < tab.blk_start[c + 1]; b += kThreads) {
+            const float2 p = partial[b];
+            A += (double)p.x;
+            N += (double)p.y;
+        }
+    }
+    A = wave_sum(A);
+    N = wave_sum(N);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) { fin_a[wave] = A; fin_n[wave] = N; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double TA = 0.0, TN = 0.0;
+        for (int w = 0; w < kThreads / kWave; ++w) { TA += fin_a[w]; TN += fin_n[w]; }
+        const float l1 = TN > 0.0 ? (float)(TA / TN) : INFINITY;
+        const int n_step = step[0];
+        uint8_t rec;
+        float f_new;
+        if (n_step < m) {
+            rec = 1; f_new = 0.f;
+        } else {
+            const float a = f[0] + l1;
+            if (a > eps) { rec = 1; f_new = 0.f; }
+            else { rec = 0; f_new = a; }
+        }
+        f[0] = f_new;
+        step[0] = n_step + 1;
+        if (l1_out) l1_out[0] = l1;
+        rec_s = rec;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < tab.n; c += kThreads)
+        if (chunk_step[c] >= 0) recompute[c] = rec_s;
+}
+
 template <int DT>
 hipError_t l1_launch(const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step, float* f,
                      uint8_t* recompute, float* l1_out, float2* partial, int m, float eps, hipStream_t s,
-                     const float* dt, void* X_next) {
+                     const float* dt, void* X_next, int rule, int32_t* gstep) {
     const int blocks = tab.blk_start[tab.n];
     if (X_next != nullptr)
         hipLaunchKernelGGL((chunk_l1_partial_kernel<DT, true>), dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1,
@@ -265,8 +322,15 @@ hipError_t l1_launch(const ChunkTable& tab, const void* X_t, const void* X_tm1, 
     else
         hipLaunchKernelGGL((chunk_l1_partial_kernel<DT, false>), dim3(blocks), dim3(kThreads), 0, s, tab, X_t, X_tm1,
                            step, partial, nullptr, nullptr);
-    hipLaunchKernelGGL(chunk_decide_kernel, dim3(tab.n), dim3(kThreads), 0, s, tab, partial, step, f, recompute,
-                       l1_out, m, eps);
+    if (rule == kRuleUniform)
+        hipLaunchKernelGGL(uniform_decide_kernel, dim3(1), dim3(kThreads), 0, s, tab, partial, step, gstep, f,
+                           recompute, l1_out, m, eps);
+    else if (rule == kRuleHistory)
+        hipLaunchKernelGGL(chunk_decide_kernel<kRuleHistory>, dim3(tab.n), dim3(kThreads), 0, s, tab, partial, step,
+                           f, recompute, l1_out, m, eps);
+    else
+        hipLaunchKernelGGL(chunk_decide_kernel<kRuleChunkwise>, dim3(tab.n), dim3(kThreads), 0, s, tab, partial,
+                           step, f, recompute, l1_out, m, eps);
     return hipGetLastError();
 }
 
@@ -280,10 +344,12 @@ int chunk_blocks_for(long long elems, int dt) {
 
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1, int32_t* step,
                            float* f, uint8_t* recompute, float* l1_out, float2* partial, int m, float eps,
-                           hipStream_t s, const float* step_dt, void* X_next) {
+                           hipStream_t s, const float* step_dt, void* X_next, int rule, int32_t* gstep) {
     if (dt == kBF16)
-        return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next);
-    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next);
+        return l1_launch<kBF16>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next,
+                                rule, gstep);
+    return l1_launch<kF32>(tab, X_t, X_tm1, step, f, recompute, l1_out, partial, m, eps, s, step_dt, X_next, rule,
+                           gstep);
 }
 
 }  // namespace fc

@@ -92,12 +92,18 @@ struct ChunkTable {
     long long off[kMaxChunks + 1];
 };
 int chunk_blocks_for(long long elems, int dt);
+// Decision rules: per chunk (FlowCache), per segment with the refresh step
+// kept in the sum (ARCache's history-guided cache), or one decision for all
+// active chunks (uniform).
+enum DecisionRule : int { kRuleChunkwise = 0, kRuleHistory = 1, kRuleUniform = 2 };
 // With X_next != nullptr, X_tm1 is the velocity v instead: the slab kernel
 // writes X_next = X_t + v * step_dt[chunk] (Euler update, rounded to the
-// storage type) and measures the L1 against it.
+// storage type) and measures the L1 against it.  Under kRuleUniform, `step`
+// is the per-chunk activity (read only), gstep [1] and f [1] the shared
+// counter and accumulator, l1_out [1].
 hipError_t launch_chunk_l1(int dt, const ChunkTable& tab, const void* X_t, const void* X_tm1,
                            int32_t* step, float* f, uint8_t* recompute, float* l1_out, float2* partial,
                            int m, float eps, hipStream_t s, const float* step_dt = nullptr,
-                           void* X_next = nullptr);
+                           void* X_next = nullptr, int rule = kRuleChunkwise, int32_t* gstep = nullptr);
 
 }  // namespace fc

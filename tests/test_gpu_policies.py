@@ -1,0 +1,143 @@
+"""GPU parity of the two other decision policies over the relative L1, in
+lockstep with the oracle (tolerances of parity.py):
+
+* fc_uniform_rel_l1_decide -- one decision for all active chunks (the
+  uniform policy the FlowCache page contrasts with);
+* fc_history_rel_l1_decide -- ARCache's History-Guided Cache rule ("Accelerating
+  Autoregressive Video Diffusion via History-Guided Cache and Residual
+  Correction", papernotes digest, Key designs item 1).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_fc_amd import synth
+from parity import EPS_BAND, L1_RTOL, DecisionLockstep
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from kv_cache_compression_fc_amd import binding
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _params(fc, cfg, n, m, eps):
+    return fc.fc_l1_params(n, m, eps, fc.FC_BF16 if cfg.dtype == "bf16" else fc.FC_F32)
+
+
+@pytest.mark.parametrize("name,eps", [("tiny", 0.15), ("stag", 0.05), ("stag", 0.02)])
+def test_history_rule_lockstep(fc, name, eps):
+    if name == "tiny":
+        cfg = synth.CHUNK_CONFIGS["tiny"]
+    else:
+        cfg = synth.ChunkConfig("stag", n_chunks=6, chunk_elems=1531, N=30, m=2, eps=(eps,), dtype="bf16",
+                                start_stride=3)
+    say(f"case: history-guided rule, {cfg.n_chunks} segments x {cfg.chunk_elems} {cfg.dtype}, delta {eps}")
+    tr = synth.ChunkTrajectory(cfg, seed=3)
+    p = _params(fc, cfg, cfg.n_chunks, cfg.m, eps)
+    ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, tr.offsets), dtype=torch.uint8, device=DEV)
+    step = torch.full((cfg.n_chunks,), -1, dtype=torch.int32, device=DEV)
+    acc = torch.zeros(cfg.n_chunks, dtype=torch.float32, device=DEV)
+    ref = torch.zeros(cfg.n_chunks, dtype=torch.uint8, device=DEV)
+    dev = torch.zeros(cfg.n_chunks, dtype=torch.float32, device=DEV)
+    lk = DecisionLockstep(cfg.n_chunks, cfg.m, eps, rule=oracle.decide_history)
+    n_ref = 0
+    for g in range(tr.n_global_steps()):
+        # over this step the history tokens move from h_{t+1} (prev) to h_t (cur)
+        h_prev, h_cur, steps = tr.pair(g)
+        step.copy_(torch.tensor(steps, dtype=torch.int32))
+        fc.fc_history_rel_l1_decide(p, tr.offsets, h_prev.to(DEV), h_cur.to(DEV), step, acc, ref, dev, ws)
+        torch.cuda.synchronize()
+        d_ref = oracle.chunk_l1_rel(h_prev, h_cur, tr.offsets)    # ||h_cur - h_prev|| / ||h_prev||
+        lk.step(steps, d_ref, ref.cpu().numpy(), acc.cpu().numpy(), dev.cpu().numpy())
+        n_ref += int(sum(ref.cpu()[i] for i in range(cfg.n_chunks) if steps[i] >= 0))
+    say(f"  decisions {lk.decisions}, refreshes {n_ref}, exempt {lk.exempt}")
+    assert 0 < n_ref < lk.decisions
+
+
+@pytest.mark.parametrize("name,eps", [("tiny", 0.01), ("stag", 0.03)])
+def test_uniform_lockstep(fc, name, eps):
+    if name == "tiny":
+        cfg = synth.CHUNK_CONFIGS["tiny"]
+    else:
+        cfg = synth.ChunkConfig("stag", n_chunks=7, chunk_elems=2049, N=25, m=3, eps=(eps,), dtype="bf16",
+                                start_stride=2)
+    say(f"case: uniform policy, {cfg.n_chunks} chunks x {cfg.chunk_elems} {cfg.dtype}, eps {eps}")
+    tr = synth.ChunkTrajectory(cfg, seed=4)
+    p = _params(fc, cfg, cfg.n_chunks, cfg.m, eps)
+    ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, tr.offsets), dtype=torch.uint8, device=DEV)
+    cstep = torch.zeros(cfg.n_chunks, dtype=torch.int32, device=DEV)
+    gstep = torch.zeros(1, dtype=torch.int32, device=DEV)
+    f = torch.zeros(1, dtype=torch.float32, device=DEV)
+    rec = torch.full((cfg.n_chunks,), 7, dtype=torch.uint8, device=DEV)
+    l1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    f_ref, n_rec, exempt = 0.0, 0, 0
+    for g in range(tr.n_global_steps()):
+        xt, xtm1, steps = tr.pair(g)
+        active = [n >= 0 for n in steps]
+        cstep.copy_(torch.tensor(steps, dtype=torch.int32))
+        rec.fill_(7)
+        fc.fc_uniform_rel_l1_decide(p, tr.offsets, xt.to(DEV), xtm1.to(DEV), cstep, gstep, f, rec, l1, ws)
+        torch.cuda.synchronize()
+        l1_ref = oracle.uniform_l1_rel(xt, xtm1, tr.offsets, active)
+        r, f_new = oracle.decide(g, f_ref, l1_ref, cfg.m, eps)
+        got_rec = rec.cpu().tolist()
+        assert gstep.item() == g + 1
+        assert abs(l1.item() - l1_ref) <= L1_RTOL * l1_ref + 1e-12, (g, l1.item(), l1_ref)
+        assert all(got_rec[i] == 7 for i in range(cfg.n_chunks) if not active[i]), "inactive flags touched"
+        flags = {got_rec[i] for i in range(cfg.n_chunks) if active[i]}
+        assert len(flags) == 1, f"step {g}: the active chunks got different decisions {got_rec}"
+        gr = flags.pop()
+        if g >= cfg.m and abs(f_ref + l1_ref - eps) <= EPS_BAND:
+            exempt += 1
+        else:
+            assert bool(gr) == r, (g, gr, r)
+            assert abs(f.item() - f_new) <= 1e-6, (g, f.item(), f_new)
+        f_ref = f_new if bool(gr) == r else f.item()
+        n_rec += gr
+    say(f"  steps {tr.n_global_steps()}, recomputes {n_rec}, exempt {exempt}")
+    assert 0 < n_rec < tr.n_global_steps()
+
+
+def test_uniform_vs_chunkwise_on_the_same_trajectory(fc):
+    # the two policies on one staggered run: the uniform one gives every
+    # active chunk the same flag, the chunkwise one decides per chunk; report
+    # both counts (the page's argument for per-chunk decisions)
+    cfg = synth.ChunkConfig("stag", n_chunks=6, chunk_elems=4096, N=30, m=3, eps=(0.02,), dtype="bf16",
+                            start_stride=5)
+    say("case: uniform vs chunkwise decisions on one staggered trajectory")
+    tr = synth.ChunkTrajectory(cfg, seed=5)
+    eps = cfg.eps[0]
+    p = _params(fc, cfg, cfg.n_chunks, cfg.m, eps)
+    ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, tr.offsets), dtype=torch.uint8, device=DEV)
+    dec = fc.ChunkDecider(tr.offsets, cfg.m, eps, torch.bfloat16, DEV)
+    cstep = torch.zeros(cfg.n_chunks, dtype=torch.int32, device=DEV)
+    gstep = torch.zeros(1, dtype=torch.int32, device=DEV)
+    f = torch.zeros(1, dtype=torch.float32, device=DEV)
+    rec = torch.zeros(cfg.n_chunks, dtype=torch.uint8, device=DEV)
+    n_chunk = n_uni = n_active = 0
+    for g in range(tr.n_global_steps()):
+        xt, xtm1, steps = tr.pair(g)
+        st = torch.tensor(steps, dtype=torch.int32)
+        dec.step.copy_(st)
+        cstep.copy_(st)
+        xt_d, xtm1_d = xt.to(DEV), xtm1.to(DEV)
+        dec.decide(xt_d, xtm1_d)
+        fc.fc_uniform_rel_l1_decide(p, tr.offsets, xt_d, xtm1_d, cstep, gstep, f, rec, None, ws)
+        torch.cuda.synchronize()
+        act = [i for i in range(cfg.n_chunks) if steps[i] >= 0]
+        n_active += len(act)
+        n_chunk += int(dec.recompute.cpu()[act].sum())
+        n_uni += int(rec.cpu()[act].sum())
+    say(f"  chunk-steps {n_active}: chunkwise recomputes {n_chunk}, uniform recomputes {n_uni}")
+    assert 0 < n_chunk < n_active and 0 < n_uni <= n_active
