@@ -1,0 +1,83 @@
+"""The library's entry points queue kernels only (no memset, copy or
+allocation), so a caller can capture them in a HIP graph.  These tests
+capture fc_kv_compress and the chunk decision, replay the graphs several
+times with eager work and synchronisations in between, and compare every
+replay bit for bit with eager calls on the same inputs."""
+import pytest
+import torch
+
+from kv_cache_compression_fc_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from kv_cache_compression_fc_amd import binding
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def test_compress_graph_replays(fc):
+    say("case: fc_kv_compress captured in a graph (H=4 d=128 bf16 Lq=300 Lk=2000 B=700), 4 replays")
+    Q, K, V = (x.to(DEV) for x in synth.random_kv(4, 300, 2000, 128, "bf16", seed=21))
+    B, lam, w = 700, 0.5, 7
+    p = fc.kv_params(Q, K, B, lam, w)
+    ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    want = fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, workspace=ws)
+    torch.cuda.synchronize()
+    out = {k: torch.empty_like(v) for k, v in want.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, out=out, workspace=ws)   # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, out=out, workspace=ws)
+    for r in range(4):
+        for v in out.values():
+            v.fill_(0)                      # eager work between replays
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in want:
+            assert torch.equal(out[k], want[k]), f"replay {r}: {k} differs from the eager call"
+
+
+def test_decision_graph_replays(fc):
+    say("case: fc_chunk_rel_l1_decide captured in a graph, 6 replays against an eager twin")
+    cfg = synth.ChunkConfig("g", n_chunks=5, chunk_elems=20000, N=12, m=2, eps=(0.05,), dtype="bf16", start_stride=0)
+    tr = synth.ChunkTrajectory(cfg, seed=8)
+    xt, xtm1, steps = tr.pair(0)
+    xt_d, xtm1_d = xt.to(DEV), xtm1.to(DEV)
+    dec = fc.ChunkDecider(tr.offsets, cfg.m, 0.05, torch.bfloat16, DEV)
+    twin = fc.ChunkDecider(tr.offsets, cfg.m, 0.05, torch.bfloat16, DEV)
+    st = torch.tensor(steps, dtype=torch.int32)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dec.decide(xt_d, xtm1_d)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.decide(xt_d, xtm1_d)
+    for d in (dec, twin):
+        d.step.copy_(st)
+        d.f.zero_()
+    torch.cuda.synchronize()
+    for r in range(6):
+        g.replay()
+        twin.decide(xt_d, xtm1_d)
+        torch.cuda.synchronize()
+        for name in ("step", "f", "recompute", "l1"):
+            assert torch.equal(getattr(dec, name), getattr(twin, name)), f"replay {r}: {name} differs"
+    # the replays advanced the device state: six steps counted from 0
+    assert dec.step.cpu().tolist() == [6] * cfg.n_chunks
