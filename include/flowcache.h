@@ -209,7 +209,7 @@ size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q);
  *   K_chunk, V_chunk [H][L_c][d] device, dtype: the chunk's keys and values,
  *                    1 <= L_c <= B_active
  *   pos0             position of the chunk's first token (its tokens get
- *                    pos0, pos0 + 1, ...; pos0 >= 0, pos0 + L_c <= 2^31 - 1)
+ *                    pos0, pos0 + 1, ...; pos0 >= 0, pos0 + L_c - 1 <= 2^31 - 1)
  *   Q [H][L_q][d]    device, dtype: the queries that score a compression;
  *                    may be NULL when the chunk fits (no compression)
  *   K_clean, V_clean [H][B_budget][d] device, dtype, in/out: the clean

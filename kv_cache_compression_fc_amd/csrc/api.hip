@@ -346,7 +346,7 @@ fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void
     fc_status st = check_cache(c);
     if (st != FC_OK) return st;
     if (L_clean == nullptr || *L_clean < 0 || *L_clean > c->B_budget) return FC_ERR_INVALID_ARG;
-    if (L_c < 1 || L_c > c->B_active || pos0 < 0 || (long long)pos0 + L_c > 0x7fffffffLL) return FC_ERR_INVALID_ARG;
+    if (L_c < 1 || L_c > c->B_active || pos0 < 0 || (long long)pos0 + L_c - 1 > 0x7fffffffLL) return FC_ERR_INVALID_ARG;
     if (!K_chunk || !V_chunk || !K_clean || !V_clean) return FC_ERR_INVALID_ARG;
     if (!aligned16(K_chunk) || !aligned16(V_chunk) || !aligned16(K_clean) || !aligned16(V_clean))
         return FC_ERR_INVALID_ARG;

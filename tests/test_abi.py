@@ -159,6 +159,7 @@ def test_cache_argument_errors(fc):
     assert commit(0, 0) == (fc.FC_ERR_INVALID_ARG, 0)
     assert commit(0, 3601) == (fc.FC_ERR_INVALID_ARG, 0)
     assert commit(0, 100, pos0=-5) == (fc.FC_ERR_INVALID_ARG, 0)
+    assert commit(0, 100, pos0=2 ** 31 - 99) == (fc.FC_ERR_INVALID_ARG, 0)   # last position would be 2^31
     assert commit(0, 100, pos0=2 ** 31 - 50) == (fc.FC_ERR_INVALID_ARG, 0)
     assert commit(0, 100, K_chunk=ctypes.c_void_p(4104)) == (fc.FC_ERR_INVALID_ARG, 0)
     assert commit(0, 100, p=_cache_params(fc, d=96)) == (fc.FC_ERR_UNSUPPORTED, 0)

@@ -106,7 +106,7 @@ def test_tiny_run(fc):
     assert ls.n_comp == cfg.n_chunks - 1
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
 def test_ragged_commits(fc, dtype, d):
     # commits of uneven sizes (tile tails, a one-token chunk, a chunk as
     # large as the active region), a first commit that already overflows
@@ -191,3 +191,26 @@ def test_magi_like_run(fc):
     torch.cuda.synchronize()
     _, ls = run_config(fc, cfg, Q, K, V, heads=heads, label="magi")
     assert ls.n_comp == cfg.n_chunks - 2
+
+
+def test_degenerate_budget_and_positions(fc):
+    # a budget of one token, single-token chunks, positions that end at 2^31 - 1
+    H, d = 2, 64
+    say("case: cache with B_budget = 1, one-token chunks, positions near 2^31")
+    cfg = synth.CacheConfig("one", H=H, d=d, n_chunks=6, fpc=1, ny=1, nx=1, B_budget=1, B_active=1, Lq=5, lam=0.5,
+                            w=3, dtype="f32")
+    Q, K, V = synth.random_kv(H, cfg.Lq, cfg.n_chunks, d, "f32", seed=12)
+    Qs = torch.stack([Q] * cfg.n_chunks)
+    run_config(fc, cfg, Qs.to(DEV), K.to(DEV), V.to(DEV), label="one")
+    # positions: the last token of the run takes position 2^31 - 1
+    cache = fc.KvCache(H, d, 4, 3, cfg.Lq, 0.5, 3, torch.float32)
+    cache.next_pos = 2 ** 31 - 1 - 5
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    cache.commit(Kd[:, :3].contiguous(), Vd[:, :3].contiguous(), Q.to(DEV))
+    cache.commit(Kd[:, 3:6].contiguous(), Vd[:, 3:6].contiguous(), Q.to(DEV))
+    torch.cuda.synchronize()
+    p = cache.pos.cpu()
+    assert cache.length == 4 and int(p.max()) <= 2 ** 31 - 1 and int(p.min()) >= 2 ** 31 - 1 - 5
+    assert all((p[h][1:] > p[h][:-1]).all() for h in range(H))
+    with pytest.raises(fc.FlowCacheError):   # one more token would pass 2^31 - 1
+        cache.commit(Kd[:, :1].contiguous(), Vd[:, :1].contiguous(), Q.to(DEV))

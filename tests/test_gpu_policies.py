@@ -141,3 +141,49 @@ def test_uniform_vs_chunkwise_on_the_same_trajectory(fc):
         n_uni += int(rec.cpu()[act].sum())
     say(f"  chunk-steps {n_active}: chunkwise recomputes {n_chunk}, uniform recomputes {n_uni}")
     assert 0 < n_chunk < n_active and 0 < n_uni <= n_active
+
+
+def test_edge_chunks_and_inactive_steps(fc):
+    # zero-length chunks, a chunk whose state is all zeros (||X_t||_1 = 0 gives
+    # +inf), and a step with every chunk inactive, under both rules
+    say("case: uniform and history rules on zero-length, zero-norm and inactive chunks")
+    offs = [0, 0, 1000, 1000, 3000, 3001]
+    x = torch.randn(3001, device=DEV).to(torch.bfloat16)
+    y = torch.randn(3001, device=DEV).to(torch.bfloat16)
+    x[1000:3000] = 0
+    p = fc.fc_l1_params(5, 1, 0.3, fc.FC_BF16)
+    ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, offs), dtype=torch.uint8, device=DEV)
+    # history rule: per-segment values
+    step = torch.tensor([0, 3, 3, 3, 3], dtype=torch.int32, device=DEV)
+    acc = torch.full((5,), 0.1, dtype=torch.float32, device=DEV)
+    ref = torch.zeros(5, dtype=torch.uint8, device=DEV)
+    dev = torch.zeros(5, dtype=torch.float32, device=DEV)
+    fc.fc_history_rel_l1_decide(p, offs, x, y, step, acc, ref, dev, ws)
+    torch.cuda.synchronize()
+    want = oracle.chunk_l1_rel(x.cpu(), y.cpu(), offs)
+    got = dev.cpu().numpy()
+    for i in range(5):
+        r, a = oracle.decide_history([0, 3, 3, 3, 3][i], 0.1, want[i], 1, 0.3)
+        assert bool(ref.cpu()[i]) == r, i
+        if np.isinf(want[i]):
+            assert np.isinf(got[i]) and np.isinf(acc.cpu()[i].item())
+        else:
+            assert abs(got[i] - want[i]) <= 1e-5 * want[i] and abs(acc.cpu()[i].item() - a) <= 1e-6
+    # uniform rule with every chunk inactive: nothing read, flags untouched,
+    # L1 over no elements is +inf, so the step recomputes
+    cstep = torch.full((5,), -1, dtype=torch.int32, device=DEV)
+    gstep = torch.tensor([4], dtype=torch.int32, device=DEV)
+    f = torch.zeros(1, dtype=torch.float32, device=DEV)
+    rec = torch.full((5,), 7, dtype=torch.uint8, device=DEV)
+    l1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fc.fc_uniform_rel_l1_decide(p, offs, x, y, cstep, gstep, f, rec, l1, ws)
+    torch.cuda.synchronize()
+    assert rec.cpu().tolist() == [7] * 5 and math.isinf(l1.item()) and gstep.item() == 5 and f.item() == 0.0
+    # uniform rule over the zero-length and zero-norm chunks and one real one
+    cstep = torch.tensor([0, 0, 0, 0, -1], dtype=torch.int32, device=DEV)
+    fc.fc_uniform_rel_l1_decide(p, offs, x, y, cstep, gstep, f, rec, l1, ws)
+    torch.cuda.synchronize()
+    want_u = oracle.uniform_l1_rel(x.cpu(), y.cpu(), offs, [True, True, True, True, False])
+    assert abs(l1.item() - want_u) <= 1e-5 * want_u
+    r, fw = oracle.decide(5, 0.0, want_u, 1, 0.3)
+    assert rec.cpu().tolist()[:4] == [int(r)] * 4 and rec.cpu()[4].item() == 7
