@@ -78,10 +78,10 @@ fc_status hip_status(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_HIP
     } while (0)
 
 // Importance (two passes) into the workspace's importance planes; with
-// imp_out they are also added up into imp_out [H][Lk].  With `r` the second
-// pass also produces the redundancy of the keys it holds (u from the
-// partials red_norm_sum left in the workspace) and the softmax partials of
-// r, one per key block.
+// imp_out they are also added up into imp_out [H][Lk].  With `r` the pass-1
+// launch also runs redundancy pass A (partials of u in the workspace), and
+// the second pass produces the redundancy of the keys it holds and the
+// softmax partials of r, one per key block.
 fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp_out,
                          void* ws, hipStream_t s, float* r = nullptr) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
@@ -91,7 +91,9 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     // one plane goes straight to imp_out when the caller wants importance
     float* planes = (imp_out && L.plan.nqs == 1) ? imp_out : at<float>(ws, L.imp);
     float* u = r ? at<float>(ws, L.u) : nullptr;
-    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s));
+    // with r, redundancy pass A runs inside the pass-1 launch
+    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s,
+                          r ? at<float>(ws, L.u_part) : nullptr, L.nbu));
     FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s,
                                 r ? at<float>(ws, L.u_part) : nullptr, L.nbu, u, p->d));
     FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, c, s, u, r,
@@ -112,10 +114,8 @@ fc_status kv_compress_run(const fc_kv_params* p, const KvLayout& L, const void* 
     float* imp = at<float>(ws, L.imp);
     float* r = at<float>(ws, L.r);
     float2* red_part = at<float2>(ws, L.red_part);
-    // redundancy pass A: partial sums of the normalised keys
-    FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(ws, L.u_part), p->H, p->L_k, s));
-    // importance (planes in the workspace); its second pass also forms r and
-    // the softmax partials of r
+    // importance (planes in the workspace): its first launch also runs
+    // redundancy pass A, its second pass forms r and the softmax partials of r
     const fc_status st = run_importance(p, L, Q, K, nullptr, ws, s, r);
     if (st != FC_OK) return st;
     // pool + score + top-B + gather

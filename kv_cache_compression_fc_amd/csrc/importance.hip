@@ -34,6 +34,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "red_rows.hpp"
 
 namespace fc {
 
@@ -198,7 +199,9 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
                                                                             const void* __restrict__ K,
                                                                             float2* __restrict__ part, int Lq,
                                                                             int Lk, int keys_per_split, int nsplit,
-                                                                            int nqb, int n_items, float c) {
+                                                                            int nqb, int n_items, float c,
+                                                                            float* __restrict__ u_part, int nbu,
+                                                                            int n_lse_blocks) {
     constexpr int kE = Elem<DT>::kBytes;
     constexpr int KT = tile_rows<DT>();
     constexpr int NKK = D / 16;
@@ -216,6 +219,19 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         else return lds2;
     };
 
+    // Workgroups past the pass-1 grid run redundancy pass A (partial sums of
+    // the normalised keys, one range of one head each): it only feeds pass 2,
+    // so it takes the slots the last round of pass 1 leaves free instead of a
+    // launch of its own before pass 1.
+    if ((int)blockIdx.x >= n_lse_blocks) {
+        const int b = (int)blockIdx.x - n_lse_blocks;
+        const int h = b / nbu, blk = b % nbu;
+        const int rows = (Lk + nbu - 1) / nbu;
+        const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
+        red_norm_sum_rows<DT, D, kThreads>(static_cast<const char*>(K) + (size_t)h * Lk * D * kE, r0, r1,
+                                           reinterpret_cast<float*>(lds0), u_part + ((size_t)h * nbu + blk) * D);
+        return;
+    }
     const int item = xcd_item((n_items + 7) / 8);
     if (item >= n_items) return;
     const int qblk = item % nqb, hs = item / nqb;
@@ -618,12 +634,15 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
 
 template <int DT, int D>
 hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq, int Lk, const ImpPlan& p,
-                      float c, hipStream_t s) {
+                      float c, hipStream_t s, float* u_part, int nbu) {
+    static_assert(kThreads / kWave * D * 4 <= SwizzledTile<DT, D, tile_rows<DT>()>::kBytes,
+                  "redundancy scratch must fit in one tile buffer");
     const int nqb = (Lq + kRowsPerBlock - 1) / kRowsPerBlock;
     const long long n_items = (long long)H * p.nsplit * nqb;
-    const int blocks = (int)((n_items + 7) / 8 * 8);
-    hipLaunchKernelGGL((imp_lse_kernel<DT, D>), dim3(blocks), dim3(kThreads), 0, s, Q, K, part, Lq, Lk,
-                       p.keys_per_split, p.nsplit, nqb, (int)n_items, c);
+    const int lse_blocks = (int)((n_items + 7) / 8 * 8);
+    const int red_blocks = u_part != nullptr ? H * nbu : 0;
+    hipLaunchKernelGGL((imp_lse_kernel<DT, D>), dim3(lse_blocks + red_blocks), dim3(kThreads), 0, s, Q, K, part, Lq,
+                       Lk, p.keys_per_split, p.nsplit, nqb, (int)n_items, c, u_part, nbu, lse_blocks);
     return hipGetLastError();
 }
 
@@ -725,11 +744,11 @@ ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d) {
 }
 
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq, int Lk,
-                          const ImpPlan& plan, float c, hipStream_t s) {
-    if (dt == kBF16) return d == 128 ? lse_launch<kBF16, 128>(Q, K, part, H, Lq, Lk, plan, c, s)
-                                     : lse_launch<kBF16, 64>(Q, K, part, H, Lq, Lk, plan, c, s);
-    return d == 128 ? lse_launch<kF32, 128>(Q, K, part, H, Lq, Lk, plan, c, s)
-                    : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s);
+                          const ImpPlan& plan, float c, hipStream_t s, float* u_part, int nbu) {
+    if (dt == kBF16) return d == 128 ? lse_launch<kBF16, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu)
+                                     : lse_launch<kBF16, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu);
+    return d == 128 ? lse_launch<kF32, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu)
+                    : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu);
 }
 
 int imp_colsum_blocks(int Lk) { return (Lk + kRowsPerBlock - 1) / kRowsPerBlock; }

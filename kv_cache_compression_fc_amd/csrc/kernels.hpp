@@ -23,8 +23,12 @@ struct ImpPlan {
     int qtiles_per_split;
 };
 ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d);
+// With u_part != nullptr the same launch also runs redundancy pass A as
+// H * nbu extra workgroups: u_part[h][b] = sum of khat over key range b of
+// head h (the ranges of launch_red_norm_sum).
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
-                          int Lk, const ImpPlan& plan, float c, hipStream_t s);
+                          int Lk, const ImpPlan& plan, float c, hipStream_t s, float* u_part = nullptr,
+                          int nbu = 0);
 // Queries padded to whole pass-2 tiles.
 int imp_lq_pad(int Lq);
 // Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled

@@ -5,91 +5,33 @@
 //     r_j = (1/L_k) sum_{i != j} khat_i . khat_j = (u . khat_j - khat_j . khat_j) / L_k,
 // so no L_k x L_k matrix is formed.  Two streaming passes over K, both
 // HBM-bound (16-byte loads, one row per TPR lanes, wave reductions):
-//   pass A: per-block partial u (fixed-order reduction, no float atomics);
+//   pass A: per-block partial u (fixed-order reduction, no float atomics;
+//           inside fc_kv_compress it runs as extra workgroups of importance
+//           pass 1 instead);
 //   pass B: u from the partials, r_j, and per-block (max, sum e^{r-max}) for
 //           the softmax over j.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "red_rows.hpp"
 
 namespace fc {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsInFlight = 4;  // rows each lane group loads before reducing
-
-// Thread layout for one row of D elements of type DT: 16 bytes per lane.
-template <int DT, int D>
-struct RowLayout {
-    static constexpr int kVec = 16 / Elem<DT>::kBytes;  // elements per lane
-    static constexpr int kTpr = D / kVec;                // lanes per row
-    static constexpr int kRpi = kThreads / kTpr;         // rows per block step
-    static_assert(kTpr <= kWave && kWave % kTpr == 0, "a row must fit in one wave");
-};
-
-template <int DT>
-__device__ __forceinline__ void load_vec(const void* p, float* x);
-template <>
-__device__ __forceinline__ void load_vec<kBF16>(const void* p, float* x) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-template <>
-__device__ __forceinline__ void load_vec<kF32>(const void* p, float* x) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
+constexpr int kRowsInFlight = kRedRowsInFlight;
+template <int DT, int D> using RL256 = RowLayout<DT, D, kThreads>;
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void red_norm_sum_kernel(const void* __restrict__ K,
                                                                 float* __restrict__ u_part, int Lk) {
-    using RL = RowLayout<DT, D>;
     constexpr int kE = Elem<DT>::kBytes;
-    __shared__ float red[RL::kRpi][D];
+    __shared__ float scratch[kThreads / kWave * D];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-
-    const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
     const int rows = (Lk + nblk - 1) / nblk;
     const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
-    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
-    float u[RL::kVec];
-#pragma unroll
-    for (int v = 0; v < RL::kVec; ++v) u[v] = 0.f;
-    for (int row = r0 + g; row < r1; row += kRowsInFlight * RL::kRpi) {
-        float x[kRowsInFlight][RL::kVec];
-#pragma unroll
-        for (int i = 0; i < kRowsInFlight; ++i) {
-            const int rr = row + i * RL::kRpi;
-            if (rr < r1) load_vec<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
-            else {
-#pragma unroll
-                for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;  // contributes nothing to u
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kRowsInFlight; ++i) {
-            float n2 = 0.f;
-#pragma unroll
-            for (int v = 0; v < RL::kVec; ++v) n2 = fmaf(x[i][v], x[i][v], n2);
-            n2 = group_sum<RL::kTpr>(n2);
-            const float inv = 1.0f / fmaxf(sqrtf(n2), 1e-12f);
-#pragma unroll
-            for (int v = 0; v < RL::kVec; ++v) u[v] = fmaf(x[i][v], inv, u[v]);
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < RL::kVec; ++v) red[g][e * RL::kVec + v] = u[v];
-    __syncthreads();
-    for (int c = threadIdx.x; c < D; c += kThreads) {
-        float acc = 0.f;
-        for (int i = 0; i < RL::kRpi; ++i) acc += red[i][c];
-        u_part[((size_t)h * nblk + blk) * D + c] = acc;
-    }
+    red_norm_sum_rows<DT, D, kThreads>(static_cast<const char*>(K) + (size_t)h * Lk * D * kE, r0, r1, scratch,
+                                       u_part + ((size_t)h * nblk + blk) * D);
 }
 
 // Online softmax statistics of a block's values, merged over the block.
@@ -118,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
                                                            const float* __restrict__ u_part, int nbu,
                                                            float* __restrict__ r, float2* __restrict__ red_part,
                                                            int Lk) {
-    using RL = RowLayout<DT, D>;
+    using RL = RL256<DT, D>;
     constexpr int kE = Elem<DT>::kBytes;
     __shared__ float ush[D];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
