@@ -2,7 +2,8 @@
 """Benchmark of the FlowCache per-step hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic inputs
-already resident in HBM:
+already resident in HBM (the two parts are independent and run on two
+streams):
   * fc_kv_compress on the MAGI-like workload (24 heads, d=128, 3600 denoising
     queries, 18000 clean keys, keep 7200 per head, lambda 0.5, pool window 7,
     bf16): importance (two MFMA passes), redundancy, pool + score + top-B,
@@ -218,9 +219,19 @@ def main() -> int:
            "V_out": torch.empty((H, Bp, d), dtype=Vd.dtype, device=dev),
            "idx": torch.empty((H, Bp), dtype=torch.int32, device=dev)}
 
+    # The two parts of a step are independent (the cache's keys vs the chunks'
+    # latents): the decision runs on a second stream (default priority),
+    # forked at the start of the step and joined at its end, so its HBM
+    # traffic overlaps the compression's compute.
+    side = torch.cuda.Stream(device=dev)
+    main = torch.cuda.current_stream()
+
     def step():
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            dec.decide(xt_d, xtm1_d, stream=side)
         fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws)
-        dec.decide(xt_d, xtm1_d)
+        main.wait_stream(side)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
