@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
 // written once, with non-temporal accesses.  With pos_out, the tokens'
 // positions follow them: pos_out[h][b] = pos[h][idx[h][b]].
 constexpr int kThreads = 256;
-constexpr int kGatherRows = 64;
+constexpr int kGatherRows = 32;  // measured 62.6 -> 60.0 us for select + gather (MAGI-like) against 64
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __restrict__ idx, int L, int Bp,
