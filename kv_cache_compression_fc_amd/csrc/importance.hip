@@ -241,6 +241,11 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
     const int half = lane >> 5;
     const FragOffsets<DT, D, KT> fo(lane);
     const int q = qblk * kRowsPerBlock + wave * 32 + (lane & 31);
+    // A wave whose 32 queries all lie past L_q (the last query block of a head
+    // is padded to kRowsPerBlock) does no arithmetic: it only issues its share
+    // of every tile load and takes every barrier, so the workgroup's barriers
+    // and waits stay the same on all waves.
+    const bool live = qblk * kRowsPerBlock + wave * 32 < Lq;
     const char* Qh = static_cast<const char*>(Q) + (size_t)h * Lq * D * kE;
     const __amdgpu_buffer_rsrc_t krs = head_rsrc(static_cast<const char*>(K) + (size_t)h * Lk * D * kE,
                                                  (uint32_t)Lk * D * kE);
@@ -267,8 +272,8 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
 
     // Shift: the maximum logit over the first 32 keys of the range (exact,
     // masked), per query.
-    float nm;
-    {
+    float nm = 0.f;
+    if (live) {
         f32x16_t acc;
         mfma_block<DT, D, KT>(acc, lds(Buf<0>{}), 0, fo, qf, NoSlice{});
         mask_rows(acc, nkeys, half);
@@ -324,21 +329,33 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         wait_vmcnt<L>();  // tile t+1 landed, tile t+2 may be in flight
         tile_barrier();
     };
+    // A padding wave's step: the same loads, waits and barrier, no arithmetic.
+    auto idle_step = [&](auto b, int t) {
+        constexpr int B = decltype(b)::value;
+        Tile::issue(krs, t + 2 < ntiles ? off0 + (uint32_t)(t + 2) * tile_bytes : kNoRecord,
+                    lds(Buf<(B + 2) % kNBuf>{}), wave, lane);
+        wait_vmcnt<L>();
+        tile_barrier();
+    };
     // Whole rounds of three tiles, then the tail: the loop's back edge then
     // only follows a buffer-2 step, so the compiler sees on every path which
     // loads the explicit waits have retired and adds no waits of its own.
-    int t = 0;
-    for (; t + 2 < ntiles; t += kNBuf) {
-        step(Buf<0>{}, t);
-        step(Buf<1>{}, t + 1);
-        step(Buf<2>{}, t + 2);
-    }
-    if (t < ntiles) {
-        step(Buf<0>{}, t);
-        if (t + 1 < ntiles) step(Buf<1>{}, t + 1);
-    }
+    auto run_tiles = [&](auto&& st) {
+        int t = 0;
+        for (; t + 2 < ntiles; t += kNBuf) {
+            st(Buf<0>{}, t);
+            st(Buf<1>{}, t + 1);
+            st(Buf<2>{}, t + 2);
+        }
+        if (t < ntiles) {
+            st(Buf<0>{}, t);
+            if (t + 1 < ntiles) st(Buf<1>{}, t + 1);
+        }
+    };
+    if (live) run_tiles(step);
+    else run_tiles(idle_step);
     wait_vmcnt<0>();
-    acc_rows(carry, 0, 16);
+    if (live) acc_rows(carry, 0, 16);
 
     float m = -nm, tot = (s0 + s1) + (s2 + s3);
     if (__syncthreads_or(!(tot < 0x1p100f))) {  // overflow (or NaN) under the fixed shift
@@ -353,6 +370,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
             for (int kb = 0; kb < KT / 32; ++kb) {
                 const int valid = nkeys - t * KT - kb * 32;
                 if (valid <= 0) break;
+                if (!live) continue;
                 f32x16_t acc;
                 mfma_block<DT, D, KT>(acc, lds(Buf<0>{}), kb * 32, fo, qf, NoSlice{});
                 mask_rows(acc, valid, half);
