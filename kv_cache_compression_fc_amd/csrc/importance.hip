@@ -302,7 +302,13 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
     f32x16_t carry;
 #pragma unroll
     for (int r = 0; r < 16; ++r) carry[r] = -INFINITY;
-    auto step = [&](auto b, int t) {
+    // A step on a tile whose rows all lie inside the range (`full`) has no
+    // masking and so no branch: the whole step is one basic block, and the
+    // scheduling barriers keep the exponentials of one block between the
+    // MFMAs of the other.  (With the masking branches in the step, the
+    // compiler moves that vector work out of the MFMA sequence.)  The last
+    // tiles of a range take the masked form.
+    auto step = [&](auto b, auto full, int t) {
         constexpr int B = decltype(b)::value;
         // Past the last tile the offset lies outside the resource: the load
         // moves no data (zeros land in a buffer nobody reads), and every step
@@ -310,46 +316,60 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         Tile::issue(krs, t + 2 < ntiles ? off0 + (uint32_t)(t + 2) * tile_bytes : kNoRecord,
                     lds(Buf<(B + 2) % kNBuf>{}), wave, lane);
         const char* buf = lds(b);
-        const int valid = nkeys - t * KT;  // rows of this tile inside the range
         f32x16_t a0;
         mfma_block<DT, D, KT>(a0, buf, 0, fo, qf, [&](int r0, int nr) { acc_rows(carry, r0, nr); });
-        if (valid < 32) mask_rows(a0, valid, half);
-        if constexpr (KT == 64) {
-            if (valid > 32) {
+        if constexpr (decltype(full)::value) {
+            if constexpr (KT == 64)
                 mfma_block<DT, D, KT>(carry, buf, 32, fo, qf, [&](int r0, int nr) { acc_rows(a0, r0, nr); });
-                if (valid < 64) mask_rows(carry, valid - 32, half);
-            } else {
-                acc_rows(a0, 0, 16);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) carry[r] = -INFINITY;
-            }
+            else
+                carry = a0;
         } else {
-            carry = a0;
+            const int valid = nkeys - t * KT;  // rows of this tile inside the range
+            if (valid < 32) mask_rows(a0, valid, half);
+            if constexpr (KT == 64) {
+                if (valid > 32) {
+                    mfma_block<DT, D, KT>(carry, buf, 32, fo, qf, [&](int r0, int nr) { acc_rows(a0, r0, nr); });
+                    if (valid < 64) mask_rows(carry, valid - 32, half);
+                } else {
+                    acc_rows(a0, 0, 16);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) carry[r] = -INFINITY;
+                }
+            } else {
+                carry = a0;
+            }
         }
         wait_vmcnt<L>();  // tile t+1 landed, tile t+2 may be in flight
         tile_barrier();
     };
     // A padding wave's step: the same loads, waits and barrier, no arithmetic.
-    auto idle_step = [&](auto b, int t) {
+    auto idle_step = [&](auto b, auto, int t) {
         constexpr int B = decltype(b)::value;
         Tile::issue(krs, t + 2 < ntiles ? off0 + (uint32_t)(t + 2) * tile_bytes : kNoRecord,
                     lds(Buf<(B + 2) % kNBuf>{}), wave, lane);
         wait_vmcnt<L>();
         tile_barrier();
     };
-    // Whole rounds of three tiles, then the tail: the loop's back edge then
-    // only follows a buffer-2 step, so the compiler sees on every path which
-    // loads the explicit waits have retired and adds no waits of its own.
+    // Whole rounds of three full tiles, then the rest (at most two full tiles
+    // and a partial one) in the masked form: the loop's back edge only
+    // follows a buffer-2 step, so the compiler sees on every path which loads
+    // the explicit waits have retired and adds no waits of its own.
+    using Full = std::true_type;
+    using Part = std::false_type;
+    const int nfull = nkeys / KT;
     auto run_tiles = [&](auto&& st) {
         int t = 0;
-        for (; t + 2 < ntiles; t += kNBuf) {
-            st(Buf<0>{}, t);
-            st(Buf<1>{}, t + 1);
-            st(Buf<2>{}, t + 2);
+        for (; t + 2 < nfull; t += kNBuf) {
+            st(Buf<0>{}, Full{}, t);
+            st(Buf<1>{}, Full{}, t + 1);
+            st(Buf<2>{}, Full{}, t + 2);
         }
         if (t < ntiles) {
-            st(Buf<0>{}, t);
-            if (t + 1 < ntiles) st(Buf<1>{}, t + 1);
+            st(Buf<0>{}, Part{}, t);
+            if (t + 1 < ntiles) {
+                st(Buf<1>{}, Part{}, t + 1);
+                if (t + 2 < ntiles) st(Buf<2>{}, Part{}, t + 2);
+            }
         }
     };
     if (live) run_tiles(step);
