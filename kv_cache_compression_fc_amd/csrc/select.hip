@@ -19,7 +19,7 @@
 // thread, staged through LDS so that every global access is coalesced; a head
 // that fits one chunk keeps its keys in LDS between the passes, a longer one
 // re-reads them from the workspace.  No global atomics: the result is
-// deterministic.  A gather kernel with one block per 64 kept rows then copies
+// deterministic.  A gather kernel with one block per 32 kept rows then copies
 // their K and V rows.
 #include <type_traits>
 
