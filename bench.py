@@ -159,6 +159,38 @@ def cache_run(fc, synth, dev, reps: int):
     }
 
 
+def other_shapes(fc, synth, dev, reps: int):
+    """fc_kv_compress alone on the SkyReels-like and long-video shapes (all
+    heads), inputs drawn on the device (seeded N(0,1) bf16; their parity at
+    these sizes is the tests' business): token-heads/s and the importance
+    rate."""
+    import torch
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for name in ("skyreels", "long"):
+        cfg = synth.KV_CONFIGS[name]
+        H, Lq, Lk, d, B = cfg.H, cfg.Lq, cfg.Lk, cfg.d, cfg.B
+        Q = torch.randn((H, Lq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        K = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        V = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        lam = 0.5
+        p = fc.kv_params(Q, K, B, lam, cfg.w)
+        ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        o = {"K_out": torch.empty((H, B, d), dtype=K.dtype, device=dev),
+             "V_out": torch.empty((H, B, d), dtype=V.dtype, device=dev),
+             "idx": torch.empty((H, B), dtype=torch.int32, device=dev)}
+        t = time_events(lambda: fc.fc_kv_compress(Q, K, V, B, lam, cfg.w, out=o, workspace=ws), max(2, reps // 2))
+        flops = 2 * 2.0 * H * Lq * Lk * d   # both importance passes
+        out[name] = {"H": H, "L_q": Lq, "L_k": Lk, "B_budget": B, "compress_ms": t,
+                     "token_heads_per_s": H * Lk / (t * 1e-3), "tokens_per_s_per_head": Lk / (t * 1e-3),
+                     "importance_executed_tflops_upper": flops / (t * 1e-3) / 1e12,
+                     "data": "device-seeded N(0,1) bf16"}
+        del Q, K, V, ws, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,7 +200,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time of the CPU-baseline (oracle) leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cache", action="store_true", help="skip the KV-cache run")
+    ap.add_argument("--no-cache", action="store_true",
+                    help="skip the KV-cache run and the SkyReels-like / long-video compressions")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
     args = ap.parse_args()
@@ -294,6 +327,12 @@ def main() -> int:
     for k, v in stages.items():
         log(f"  {k}: {v}")
 
+    others = None
+    if not args.no_cache:
+        others = other_shapes(fc, synth, dev, reps)
+        for k, v in others.items():
+            log(f"  {k}: {v}")
+
     cache = None
     if not args.no_cache:
         cache = cache_run(fc, synth, dev, reps)
@@ -336,6 +375,8 @@ def main() -> int:
     }
     if cache is not None:
         result["cache"] = cache
+    if others is not None:
+        result["other_shapes"] = others
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on whole steps")
         result["cpu_baseline"] = cpu_baseline(cfg, ccfg, args.cpu_seconds)
