@@ -19,7 +19,8 @@
  *   - Pointers named as device pointers must point to memory of the current
  *     HIP device; host pointers are read before the call returns.
  *   - The caller owns all memory.  The library never allocates or frees; any
- *     temporary storage is the caller's workspace, sized by the *_bytes query.
+ *     temporary storage is the caller's workspace, sized by the *_bytes query
+ *     and 256-byte aligned (as every hipMalloc or torch allocation is).
  *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
  *     and runs asynchronously.  Argument checks happen on the host, before
  *     anything is queued, and return an error code synchronously.
@@ -27,9 +28,10 @@
  *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
  *     in [0,1], even pool window, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
  *     128, unknown dtype, more than 65535 heads, one head's Q or K rows at
- *     2 GiB or more, too many chunks), FC_ERR_WORKSPACE (workspace null or
- *     smaller than the query), FC_ERR_HIP (a launch failed).  No exception
- *     crosses the ABI.  NaN/Inf inputs are not supported.
+ *     2 GiB or more, too many chunks), FC_ERR_WORKSPACE (workspace null,
+ *     not 256-byte aligned or smaller than the query), FC_ERR_HIP (a launch
+ *     failed).  No exception crosses the ABI.  NaN/Inf inputs are not
+ *     supported.
  *   - The library keeps no state between calls; calls on different streams
  *     with different workspaces may run concurrently.
  */

@@ -16,6 +16,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A usable workspace: present, large enough, and 256-byte aligned (every
+// buffer carved from it sits at a 256-byte offset).
+bool ws_ok(const void* ws, size_t bytes, size_t need) {
+    return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0 && bytes >= need;
+}
+
 // ---- KV compression -------------------------------------------------------------------
 struct KvLayout {
     ImpPlan plan;
@@ -220,7 +226,7 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
         return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     return kv_compress_run(p, L, Q, K, V, K_out, V_out, idx_out, score_out, imp_pooled_out, red_out, workspace,
                            static_cast<hipStream_t>(stream));
 }
@@ -231,7 +237,7 @@ fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, 
     if (st != FC_OK) return st;
     if (!Q || !K || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -241,7 +247,7 @@ fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void*
     if (st != FC_OK) return st;
     if (!Q || !K || !lse_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float2* part = at<float2>(workspace, L.part);
@@ -256,7 +262,7 @@ fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const vo
     if (st != FC_OK) return st;
     if (!Q || !K || !lse || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float* nlse2 = at<float>(workspace, L.nlse2);
@@ -273,7 +279,7 @@ fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, v
     if (st != FC_OK) return st;
     if (!K || !r_out || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     FC_TRY(launch_red_norm_sum(dt, p->d, K, at<float>(workspace, L.u_part), p->H, p->L_k, s));
@@ -293,7 +299,7 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
     if (gather && (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out)))
         return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
-    if (workspace == nullptr || workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
@@ -315,7 +321,7 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
     if (H < 1 || L < 1 || B < 1 || !scores || !idx_out) return FC_ERR_INVALID_ARG;
     if (H > 65535) return FC_ERR_UNSUPPORTED;
     const size_t need = fc_topb_select_workspace_bytes(H, L);
-    if (workspace == nullptr || workspace_bytes < need) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, need)) return FC_ERR_WORKSPACE;
     const int Bp = B < L ? B : L;
     FC_TRY(launch_sel_head(scores, 1, nullptr, nullptr, 0, 0.f, 1, nullptr, nullptr, nullptr,
                            static_cast<uint32_t*>(workspace), H, L, Bp, idx_out, static_cast<hipStream_t>(stream)));
@@ -369,7 +375,7 @@ fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void
     if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
     const CacheLayout CL = cache_layout(c);
     const KvLayout KL = kv_layout(&kp);
-    if (workspace == nullptr || workspace_bytes < CL.comp + KL.total) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, CL.comp + KL.total)) return FC_ERR_WORKSPACE;
     void* Km = at<char>(workspace, CL.Km);
     void* Vm = at<char>(workspace, CL.Vm);
     int32_t* pm = pos_clean ? at<int32_t>(workspace, CL.pm) : nullptr;
@@ -396,7 +402,7 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
     if (st != FC_OK) return st;
     if (!X_t || !X_tm1 || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
     if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
-    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, chunk_ws_bytes(tab))) return FC_ERR_WORKSPACE;
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, step, f, recompute, l1_rel_out,
                                       static_cast<float2*>(workspace), p->m, p->eps,
@@ -412,7 +418,7 @@ fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_of
     if (st != FC_OK) return st;
     if (!X_t || !v || !dt || !X_next || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
     if (!aligned16(X_t) || !aligned16(v) || !aligned16(X_next)) return FC_ERR_INVALID_ARG;
-    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, chunk_ws_bytes(tab))) return FC_ERR_WORKSPACE;
     const int dtp = p->dtype == FC_BF16 ? kBF16 : kF32;
     return hip_status(launch_chunk_l1(dtp, tab, X_t, v, step, f, recompute, l1_rel_out,
                                       static_cast<float2*>(workspace), p->m, p->eps,
@@ -428,7 +434,7 @@ fc_status fc_uniform_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_o
     if (st != FC_OK) return st;
     if (!X_t || !X_tm1 || !chunk_step || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
     if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
-    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, chunk_ws_bytes(tab))) return FC_ERR_WORKSPACE;
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, const_cast<int32_t*>(chunk_step), f, recompute,
                                       l1_rel_out, static_cast<float2*>(workspace), p->m, p->eps,
@@ -443,7 +449,7 @@ fc_status fc_history_rel_l1_decide(const fc_l1_params* p, const int64_t* segment
     if (st != FC_OK) return st;
     if (!h_prev || !h_cur || !step || !acc || !refresh) return FC_ERR_INVALID_ARG;
     if (!aligned16(h_prev) || !aligned16(h_cur)) return FC_ERR_INVALID_ARG;
-    if (workspace == nullptr || workspace_bytes < chunk_ws_bytes(tab)) return FC_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, chunk_ws_bytes(tab))) return FC_ERR_WORKSPACE;
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     // ||h_t - h_{t+1}||_1 / ||h_{t+1}||_1: the previous state takes the
     // denominator's place, the first argument of the slab pass

@@ -81,6 +81,10 @@ def test_kv_argument_errors(fc):
     st = lib.fc_kv_compress(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, None, None, None, ws,
                             need - 1, None)
     assert st == fc.FC_ERR_WORKSPACE
+    # misaligned workspace
+    st = lib.fc_kv_compress(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, None, None, None,
+                            ctypes.c_void_p(4096 + 128), need, None)
+    assert st == fc.FC_ERR_WORKSPACE
     # unsupported head dim / dtype
     st = lib.fc_kv_compress(ctypes.byref(_params(fc, d=96)), dummy, dummy, dummy, dummy, dummy, dummy, None, None,
                             None, ws, need, None)
