@@ -32,8 +32,9 @@
  *     not 256-byte aligned or smaller than the query), FC_ERR_HIP (a launch
  *     failed).  No exception crosses the ABI.  NaN/Inf inputs are not
  *     supported.
- *   - The library keeps no state between calls; calls on different streams
- *     with different workspaces may run concurrently.
+ *   - The library keeps no state between calls (apart from a per-device
+ *     cache of the importance kernels' occupancy, filled on first use); calls
+ *     on different streams with different workspaces may run concurrently.
  */
 #ifndef FLOWCACHE_H
 #define FLOWCACHE_H
