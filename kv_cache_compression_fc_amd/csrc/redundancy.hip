@@ -62,12 +62,30 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
                                                            int Lk) {
     using RL = RL256<DT, D>;
     constexpr int kE = Elem<DT>::kBytes;
+    constexpr int kParts = kThreads / D;  // threads per column of u
+    __shared__ float upart[kParts][D];
     __shared__ float ush[D];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-    for (int c = threadIdx.x; c < D; c += kThreads) {
+    // u = sum of the nbu partials: every thread takes every kParts-th partial
+    // of one column (two independent sums), then the parts are added in order
+    {
+        const int c = threadIdx.x % D, part = threadIdx.x / D;
+        const float* pc = u_part + (size_t)h * nbu * D + c;
+        float a0 = 0.f, a1 = 0.f;
+        int i = part;
+        for (; i + kParts < nbu; i += 2 * kParts) {
+            a0 += pc[(size_t)i * D];
+            a1 += pc[(size_t)(i + kParts) * D];
+        }
+        if (i < nbu) a0 += pc[(size_t)i * D];
+        upart[part][c] = a0 + a1;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
         float acc = 0.f;
-        for (int i = 0; i < nbu; ++i) acc += u_part[((size_t)h * nbu + i) * D + c];
-        ush[c] = acc;
+#pragma unroll
+        for (int q = 0; q < kParts; ++q) acc += upart[q][threadIdx.x];
+        ush[threadIdx.x] = acc;
     }
     __syncthreads();
     const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
@@ -79,7 +97,9 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
     const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
     const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
     const float inv_lk = 1.0f / (float)Lk;
-    float m = -1e30f, s = 0.f;  // base-2 running stats of r * log2e
+    // r_j is a mean of cosines, |r_j| < 1, so sum 2^(r_j log2e - log2e) needs
+    // no running maximum: the block's softmax partial is (log2e, s)
+    float s = 0.f;
     for (int row = r0 + g; row < r1; row += kRowsInFlight * RL::kRpi) {
         float x[kRowsInFlight][RL::kVec];
 #pragma unroll
@@ -106,11 +126,11 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
             const float rj = (dot * inv - n2 * inv * inv) * inv_lk;
             if (e == 0 && rr < r1) {
                 r[(size_t)h * Lk + rr] = rj;
-                lse2_merge(m, s, rj * kLog2e, 1.0f);
+                s += exp2_hw(fmaf(rj, kLog2e, -kLog2e));
             }
         }
     }
-    block_softmax_stats(m, s, red_part + (size_t)h * nblk + blk);
+    block_softmax_stats(kLog2e, s, red_part + (size_t)h * nblk + blk);
 }
 
 __global__ __launch_bounds__(kThreads) void red_stats_kernel(const float* __restrict__ r,
@@ -143,8 +163,8 @@ int red_nbu(int Lk) {
     return n < 1 ? 1 : (n > 64 ? 64 : n);
 }
 int red_nbr(int Lk) {
-    int n = (Lk + 127) / 128;
-    return n < 1 ? 1 : (n > 128 ? 128 : n);
+    int n = (Lk + 255) / 256;
+    return n < 1 ? 1 : (n > 64 ? 64 : n);
 }
 
 hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, hipStream_t s) {
