@@ -28,7 +28,8 @@
  *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
  *     in [0,1], even pool window, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
  *     128, unknown dtype, more than 65535 heads, one head's Q or K rows at
- *     2 GiB or more, too many chunks), FC_ERR_WORKSPACE (workspace null,
+ *     2 GiB or more, launch grids beyond a dispatch's 32-bit work-item
+ *     count, too many chunks), FC_ERR_WORKSPACE (workspace null,
  *     not 256-byte aligned or smaller than the query), FC_ERR_HIP (a launch
  *     failed).  No exception crosses the ABI.  NaN/Inf inputs are not
  *     supported.

@@ -27,6 +27,7 @@ struct KvLayout {
     ImpPlan plan;
     int nbu, nbr;
     int nkb;  // importance pass-2 workgroups per head (redundancy softmax partials of the fused path)
+    bool fits;  // every launch of the plan fits a dispatch
     size_t part, nlse2, imp, r, u_part, u, red_part, keys, total;
 };
 
@@ -53,6 +54,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.nbu = red_nbu(p->L_k);
     L.nbr = red_nbr(p->L_k);
     L.nkb = imp_colsum_blocks(p->L_k);
+    L.fits = imp_grids_fit(p->H, p->L_q, p->L_k, L.plan, L.nbu);
     const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
@@ -214,7 +216,8 @@ const char* fc_status_string(fc_status s) {
 
 size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p) {
     if (check_kv(p) != FC_OK) return 0;
-    return kv_layout(p).total;
+    const KvLayout L = kv_layout(p);
+    return L.fits ? L.total : 0;
 }
 
 fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, const void* V, void* K_out,
@@ -226,6 +229,7 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
         return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     return kv_compress_run(p, L, Q, K, V, K_out, V_out, idx_out, score_out, imp_pooled_out, red_out, workspace,
                            static_cast<hipStream_t>(stream));
@@ -237,6 +241,7 @@ fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, 
     if (st != FC_OK) return st;
     if (!Q || !K || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream));
 }
@@ -247,6 +252,7 @@ fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void*
     if (st != FC_OK) return st;
     if (!Q || !K || !lse_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
@@ -262,6 +268,7 @@ fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const vo
     if (st != FC_OK) return st;
     if (!Q || !K || !lse || !imp_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
@@ -279,6 +286,7 @@ fc_status fc_kv_redundancy(const fc_kv_params* p, const void* K, float* r_out, v
     if (st != FC_OK) return st;
     if (!K || !r_out || !aligned16(K)) return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
@@ -299,6 +307,7 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
     if (gather && (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out)))
         return FC_ERR_INVALID_ARG;
     const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
@@ -339,7 +348,9 @@ size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q) {
         const int32_t Lk = (int32_t)(L < hi ? L : hi);
         const fc_kv_params p = cache_kv_params(c, L_q, Lk);
         if (check_kv(&p) != FC_OK) return 0;
-        const size_t t = kv_layout(&p).total;
+        const KvLayout KL = kv_layout(&p);
+        if (!KL.fits) return 0;
+        const size_t t = KL.total;
         comp = t > comp ? t : comp;
         if (Lk >= hi) break;
     }
@@ -375,6 +386,7 @@ fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void
     if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
     const CacheLayout CL = cache_layout(c);
     const KvLayout KL = kv_layout(&kp);
+    if (!KL.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, CL.comp + KL.total)) return FC_ERR_WORKSPACE;
     void* Km = at<char>(workspace, CL.Km);
     void* Vm = at<char>(workspace, CL.Vm);

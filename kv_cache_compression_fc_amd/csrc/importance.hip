@@ -791,6 +791,14 @@ hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* p
 
 int imp_colsum_blocks(int Lk) { return (Lk + kRowsPerBlock - 1) / kRowsPerBlock; }
 
+bool imp_grids_fit(int H, int Lq, int Lk, const ImpPlan& p, int nbu) {
+    // one-dimensional grids: a dispatch counts its work-items in 32 bits
+    const long long nqb = (Lq + kRowsPerBlock - 1) / kRowsPerBlock;
+    const long long lse = ((long long)H * p.nsplit * nqb + 7) / 8 * 8 + (long long)H * nbu;
+    const long long col = ((long long)H * p.nqs * imp_colsum_blocks(Lk) + 7) / 8 * 8;
+    return lse * kThreads < (1LL << 32) && col * kThreads < (1LL << 32);
+}
+
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
                              int Lq, int Lk, const ImpPlan& p, float c, hipStream_t s, const float* u, float* r,
                              float2* red_part) {

@@ -38,6 +38,9 @@ int imp_lq_pad(int Lq);
 // it holds and one softmax partial (max, sum e^{r-max}, base 2) per key
 // block into red_part [H][imp_colsum_blocks(Lk)].
 int imp_colsum_blocks(int Lk);
+// Whether both importance launches of this plan (pass 1 with nbu redundancy
+// workgroups per head) fit a dispatch's 32-bit work-item count.
+bool imp_grids_fit(int H, int Lq, int Lk, const ImpPlan& plan, int nbu);
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
                              int Lq, int Lk, const ImpPlan& plan, float c, hipStream_t s, const float* u = nullptr,
                              float* r = nullptr, float2* red_part = nullptr);

@@ -62,6 +62,8 @@ def test_kv_workspace_query(fc):
     for bad in (dict(H=0), dict(L_k=0), dict(B_budget=0), dict(lambda_=1.5), dict(lambda_=float("nan")),
                 dict(pool_window=4), dict(pool_window=0), dict(softmax_scale=-1.0), dict(d=96), dict(dtype=7)):
         assert fc.fc_kv_compress_workspace_bytes(_params(fc, **bad)) == 0, bad
+    # more work-items than one dispatch can count (65535 heads of 8M queries)
+    assert fc.fc_kv_compress_workspace_bytes(_params(fc, H=65535, L_q=8_000_000, L_k=64, B_budget=8)) == 0
 
 
 def test_kv_argument_errors(fc):
