@@ -190,7 +190,7 @@ fc_status chunk_table(const fc_l1_params* p, const int64_t* off, ChunkTable* tab
         tab->off[i] = off[i];
         tab->blk_start[i] = (int32_t)blocks;
         blocks += chunk_blocks_for(off[i + 1] - off[i], dt);
-        if (blocks > 0x7fffffffLL) return FC_ERR_UNSUPPORTED;
+        if (blocks > 0xffffffffLL / 256) return FC_ERR_UNSUPPORTED;  // the slab grid's work-items fit 32 bits
     }
     tab->off[p->n_chunks] = off[p->n_chunks];
     tab->blk_start[p->n_chunks] = (int32_t)blocks;
