@@ -2,7 +2,8 @@
 allocation), so a caller can capture them in a HIP graph.  These tests
 capture fc_kv_compress and the chunk decision, replay the graphs several
 times with eager work and synchronisations in between, and compare every
-replay bit for bit with eager calls on the same inputs."""
+replay bit for bit with eager calls on the same inputs; and it runs calls on
+two streams at once, each with its own workspace."""
 import pytest
 import torch
 
@@ -81,3 +82,39 @@ def test_decision_graph_replays(fc):
             assert torch.equal(getattr(dec, name), getattr(twin, name)), f"replay {r}: {name} differs"
     # the replays advanced the device state: six steps counted from 0
     assert dec.step.cpu().tolist() == [6] * cfg.n_chunks
+
+
+def test_concurrent_streams(fc):
+    # calls on different streams with their own workspaces may overlap: two
+    # compressions and two decisions in flight at once give the results of
+    # the same calls made one after the other
+    say("case: fc_kv_compress and the chunk decision on two streams at once")
+    Q, K, V = (x.to(DEV) for x in synth.random_kv(3, 257, 3001, 128, "bf16", seed=31))
+    Q2, K2, V2 = (x.to(DEV) for x in synth.random_kv(3, 257, 3001, 128, "bf16", seed=32))
+    want1 = fc.fc_kv_compress(Q, K, V, 1000, 0.4, 7, want_scores=True)
+    want2 = fc.fc_kv_compress(Q2, K2, V2, 1000, 0.6, 5, want_scores=True)
+    cfg = synth.ChunkConfig("s", n_chunks=4, chunk_elems=50000, N=8, m=1, eps=(0.05,), dtype="bf16", start_stride=0)
+    tr = synth.ChunkTrajectory(cfg, seed=9)
+    xt, xtm1, steps = tr.pair(2)
+    xt_d, xtm1_d = xt.to(DEV), xtm1.to(DEV)
+    ref = fc.ChunkDecider(tr.offsets, cfg.m, 0.05, torch.bfloat16, DEV)
+    ref.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    ref.decide(xt_d, xtm1_d)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    dec = fc.ChunkDecider(tr.offsets, cfg.m, 0.05, torch.bfloat16, DEV)
+    dec.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            got1 = fc.fc_kv_compress(Q, K, V, 1000, 0.4, 7, want_scores=True, stream=s1)
+        with torch.cuda.stream(s2):
+            got2 = fc.fc_kv_compress(Q2, K2, V2, 1000, 0.6, 5, want_scores=True, stream=s2)
+            dec.step.copy_(torch.tensor(steps, dtype=torch.int32, device=DEV))
+            dec.f.zero_()
+            dec.decide(xt_d, xtm1_d, stream=s2)
+        torch.cuda.synchronize()
+        for k in want1:
+            assert torch.equal(got1[k], want1[k]) and torch.equal(got2[k], want2[k]), k
+        for name in ("f", "recompute", "l1", "step"):
+            assert torch.equal(getattr(dec, name), getattr(ref, name)), name
