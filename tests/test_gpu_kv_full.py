@@ -6,7 +6,8 @@ heads (heads are independent, so each sampled head is checked whole).
 The MAGI-like case runs the benchmark's own inputs.  For the two larger ones
 the sampled heads carry the smooth-field generator's values and the other
 heads seeded N(0,1) values drawn on the device: every head differs, so a head
-mix-up still shows, and the oracle is spent only where it is compared.
+mix-up still shows, and the oracle is spent only where it is compared.  The
+last case takes heads of the largest size the boundary accepts.
 """
 import math
 
@@ -102,3 +103,46 @@ def test_full_long_video_lambda_sweep(fc):
     (s0, s1), (d0, d1) = cfg.dup
     red = out["red"][heads[0]]
     assert torch.equal(red[s0 * tpf:s1 * tpf], red[d0 * tpf:d1 * tpf])
+
+
+@pytest.mark.timeout(900)
+def test_heads_at_the_32bit_byte_limit(fc):
+    # One head's rows are addressed with 32-bit byte offsets, so a head may
+    # hold up to 2^31 - 1 bytes: here 8,388,607 bf16 keys of d = 128
+    # (2^31 - 256 bytes) in each of two heads, the second starting past 2 GiB.
+    # Copies of the queries are planted as keys at both ends of every head:
+    # each gets far more attention than a random key (about 2000 times the
+    # mean importance) without swamping the others, so they are kept, the
+    # gather reads rows at the very end of each head, and the rest of the
+    # selection still has a spread of importance to order.
+    H, Lq, d, B, lam, w = 2, 24, 128, 7000, 0.5, 7
+    Lk = (2 ** 31 - 1) // (d * 2)
+    p = fc.fc_kv_params(H, d, Lq, Lk, B, lam, w, 0.0, fc.FC_BF16)
+    assert fc.fc_kv_compress_workspace_bytes(p) > 0
+    p.L_k = Lk + 1  # one row more is 2^31 bytes: refused
+    assert fc.fc_kv_compress_workspace_bytes(p) == 0
+    say(f"case: H={H} Lq={Lq} Lk={Lk} (2^31 - 256 bytes per head) B={B} bf16")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    Qd = torch.randn((H, Lq, d), generator=g, device=DEV).to(torch.bfloat16)
+    Kd = torch.empty((H, Lk, d), dtype=torch.bfloat16, device=DEV)
+    for h in range(H):  # fp32 temporaries of one head at a time
+        Kd[h].copy_(torch.randn((Lk, d), generator=g, device=DEV))
+    Kd[:, :Lq] = Qd
+    Kd[:, Lk - Lq:] = Qd
+    Vd = torch.empty_like(Kd)
+    for h in range(H):
+        Vd[h].copy_(torch.randn((Lk, d), generator=g, device=DEV))
+    out = fc.fc_kv_compress(Qd, Kd, Vd, B, lam, w, want_scores=True)
+    torch.cuda.synchronize()
+    ends = out["idx"][:, -Lq:].cpu()
+    assert torch.equal(ends, torch.arange(Lk - Lq, Lk, dtype=torch.int32).expand(H, Lq)), "planted end rows not kept"
+    say("  GPU done; oracle")
+    Q, K = Qd.cpu(), Kd.cpu()
+    imp = oracle.importance(Q, K, 1.0 / math.sqrt(d))
+    r = oracle.redundancy_mean(K)
+    del K
+    imp_p = oracle.maxpool1d(imp, w)
+    red = oracle.softmax_lastdim(r)
+    ref = {"imp_pooled": imp_p, "red": red, "score": oracle.joint_score(imp_p, red, lam)}
+    check_heads(out, ref, lam, B, Kd, Vd, list(range(H)), "32-bit limit")
