@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+import parity
 from kv_cache_compression_fc_amd import synth
 from parity import DecisionLockstep as Lockstep
 
@@ -134,3 +135,76 @@ def test_repeated_calls_share_workspace(fc):
     torch.cuda.synchronize()
     assert dec.step.cpu().tolist() == [20] * n
     np.testing.assert_allclose(dec.l1.cpu().numpy(), ref, rtol=1e-5)
+
+
+@pytest.mark.timeout(600)
+def test_chunk_beyond_2pow31_elements(fc):
+    # Chunk offsets are int64 element counts: one chunk of more than 2^31 bf16
+    # elements (4.3 GB per state), starting at an unaligned element, between
+    # two small chunks; the plain decision and then the fused Euler step on
+    # the same chunks, in place.  The oracle runs on slices of at most 2^28
+    # elements of one chunk each; their fp64 sums add up per chunk.
+    sizes = [1003, 2 ** 31 + 12345, 7]
+    offs = [0]
+    for s in sizes:
+        offs.append(offs[-1] + s)
+    total = offs[-1]
+    piece = 1 << 28
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    say(f"case: chunks of {sizes} bf16 elements (offsets {offs})")
+
+    def fill(x, base, scales):
+        # x = base + scale_c * N(0,1) per chunk c, written piece by piece
+        for c in range(len(sizes)):
+            for lo in range(offs[c], offs[c + 1], piece):
+                hi = min(offs[c + 1], lo + piece)
+                y = torch.randn(hi - lo, generator=g, device=DEV) * scales[c]
+                if base is not None:
+                    y += base[lo:hi].float()
+                x[lo:hi].copy_(y)
+        return x
+
+    xt = fill(torch.empty(total, dtype=torch.bfloat16, device=DEV), None, (1.0, 1.0, 1.0))
+    xtm1 = fill(torch.empty_like(xt), xt, (0.001, 0.01, 0.5))
+    eps, m = 0.005, 0
+    dec = fc.ChunkDecider(offs, m, eps, torch.bfloat16, DEV)
+    dec.step.zero_()
+    dec.decide(xt, xtm1)
+    torch.cuda.synchronize()
+
+    A, N = np.zeros(len(sizes)), np.zeros(len(sizes))
+    for c in range(len(sizes)):
+        for lo in range(offs[c], offs[c + 1], piece):
+            hi = min(offs[c + 1], lo + piece)
+            a, n = oracle.chunk_l1_sums(xt[lo:hi].cpu(), xtm1[lo:hi].cpu(), [0, hi - lo])
+            A[c] += a[0]
+            N[c] += n[0]
+    l1_ref = A / N
+    got = dec.l1.cpu().numpy()
+    say(f"  l1 {got.tolist()} oracle {l1_ref.tolist()}")
+    np.testing.assert_allclose(got, l1_ref, rtol=1e-5)
+    for c in range(len(sizes)):
+        want, _ = oracle.decide(0, 0.0, l1_ref[c], m, eps)
+        if abs(l1_ref[c] - eps) > parity.EPS_BAND:
+            assert int(dec.recompute[c]) == int(want), c
+    del xtm1
+
+    # fused Euler step, in place on a copy of X_t
+    v = fill(torch.empty_like(xt), None, (1.0, 1.0, 1.0))
+    dts = [-0.001, -0.01, -0.2]
+    x_work = xt.clone()
+    fused = fc.ChunkDecider(offs, m, eps, torch.bfloat16, DEV)
+    fused.step.zero_()
+    fused.euler_step(x_work, v, torch.tensor(dts, dtype=torch.float32, device=DEV), x_work)
+    plain = fc.ChunkDecider(offs, m, eps, torch.bfloat16, DEV)
+    plain.step.zero_()
+    plain.decide(xt, x_work)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.l1.cpu(), plain.l1.cpu()) and torch.equal(fused.recompute.cpu(), plain.recompute.cpu())
+    # the stored update, bit for bit, on ranges at the start, across 2^31 and
+    # across the last chunk border
+    for lo, hi in ((0, 1 << 20), (2 ** 31 - (1 << 20), 2 ** 31 + (1 << 20)), (offs[2] - (1 << 20), total)):
+        rel = [0] + [min(max(o - lo, 0), hi - lo) for o in offs[1:-1]] + [hi - lo]
+        ref = oracle.euler_step(xt[lo:hi].cpu(), v[lo:hi].cpu(), rel, dts, [True] * len(sizes))
+        assert torch.equal(x_work[lo:hi].cpu(), ref), (lo, hi)
