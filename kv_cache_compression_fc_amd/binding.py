@@ -123,6 +123,32 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype=None) -> None:
+    """The library reads and writes exactly the extents its arguments imply;
+    a tensor of another shape or dtype would be accessed out of bounds, so it
+    is refused here, before any pointer crosses the boundary."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_flat(name: str, t: Optional[torch.Tensor], min_numel: int, dtype) -> None:
+    """A flat state: any shape, at least min_numel elements of dtype."""
+    if t is None:
+        return
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the offsets need {min_numel}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == FC_BF16 else torch.float32
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -139,7 +165,11 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def kv_params(Q: torch.Tensor, K: torch.Tensor, B_budget: int, lam: float, pool_window: int,
               softmax_scale: float = 0.0) -> fc_kv_params:
+    """Parameters of Q [H][L_q][d] and K [H][L_k][d] (same dtype)."""
+    if Q.dim() != 3 or K.dim() != 3:
+        raise ValueError("Q and K must be [H][L][d]")
     H, Lq, d = Q.shape
+    _expect("K", K, (H, K.shape[1], d), Q.dtype)
     return fc_kv_params(H, d, Lq, K.shape[1], int(B_budget), float(lam), int(pool_window),
                         float(softmax_scale), _dtype_code(K))
 
@@ -170,6 +200,12 @@ def fc_kv_compress(Q, K, V, B_budget: int, lam: float, pool_window: int, softmax
     if want_scores:
         for k in ("score", "imp_pooled", "red"):
             out.setdefault(k, torch.empty((H, Lk), dtype=torch.float32, device=dev))
+    _expect("V", V, (H, Lk, d), K.dtype)
+    for k in ("K_out", "V_out"):
+        _expect(k, out[k], (H, Bp, d), K.dtype)
+    _expect("idx", out["idx"], (H, Bp), torch.int32)
+    for k in ("score", "imp_pooled", "red"):
+        _expect(k, out.get(k), (H, Lk), torch.float32)
     nbytes = fc_kv_compress_workspace_bytes(p)
     ws = _workspace(nbytes, dev, workspace)
     _check("fc_kv_compress", _lib.fc_kv_compress(
@@ -184,6 +220,7 @@ def fc_kv_importance(Q, K, softmax_scale: float = 0.0, imp_out=None, workspace=N
     H, Lk, _ = K.shape
     if imp_out is None:
         imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    _expect("imp_out", imp_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance", _lib.fc_kv_importance(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(imp_out), _ptr(ws),
                                                      ws.numel(), _stream(stream)))
@@ -195,6 +232,7 @@ def fc_kv_importance_lse(Q, K, softmax_scale: float = 0.0, lse_out=None, workspa
     H, Lq, _ = Q.shape
     if lse_out is None:
         lse_out = torch.empty((H, Lq), dtype=torch.float32, device=Q.device)
+    _expect("lse_out", lse_out, (H, Lq), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance_lse", _lib.fc_kv_importance_lse(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse_out),
                                                              _ptr(ws), ws.numel(), _stream(stream)))
@@ -206,6 +244,8 @@ def fc_kv_importance_colsum(Q, K, lse, softmax_scale: float = 0.0, imp_out=None,
     H, Lk, _ = K.shape
     if imp_out is None:
         imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    _expect("lse", lse, (H, Q.shape[1]), torch.float32)
+    _expect("imp_out", imp_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance_colsum", _lib.fc_kv_importance_colsum(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse),
                                                                    _ptr(imp_out), _ptr(ws), ws.numel(),
@@ -218,6 +258,7 @@ def fc_kv_redundancy(K, r_out=None, workspace=None, stream=None) -> torch.Tensor
     p = fc_kv_params(H, d, 1, Lk, 1, 0.5, 1, 0.0, _dtype_code(K))
     if r_out is None:
         r_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    _expect("r_out", r_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_redundancy", _lib.fc_kv_redundancy(ctypes.byref(p), _ptr(K), _ptr(r_out), _ptr(ws), ws.numel(),
                                                      _stream(stream)))
@@ -227,7 +268,13 @@ def fc_kv_redundancy(K, r_out=None, workspace=None, stream=None) -> torch.Tensor
 def fc_kv_select(imp, r, B_budget: int, lam: float, pool_window: int, K=None, V=None, want_scores: bool = True,
                  workspace=None, stream=None) -> Dict[str, torch.Tensor]:
     H, Lk = imp.shape
+    _expect("r", r, (H, Lk), torch.float32)
+    _expect("imp", imp, (H, Lk), torch.float32)
+    if (K is None) != (V is None):
+        raise ValueError("K and V are given together or not at all")
     d = K.shape[2] if K is not None else 64
+    _expect("K", K, (H, Lk, d))
+    _expect("V", V, (H, Lk, d), K.dtype if K is not None else None)
     dt = _dtype_code(K) if K is not None else FC_F32
     p = fc_kv_params(H, d, 1, Lk, int(B_budget), float(lam), int(pool_window), 0.0, dt)
     Bp = min(int(B_budget), Lk)
@@ -253,8 +300,10 @@ def fc_topb_select_workspace_bytes(H: int, L: int) -> int:
 
 def fc_topb_select(scores: torch.Tensor, B: int, idx_out=None, workspace=None, stream=None) -> torch.Tensor:
     H, L = scores.shape
+    _expect("scores", scores, (H, L), torch.float32)
     if idx_out is None:
         idx_out = torch.empty((H, min(int(B), L)), dtype=torch.int32, device=scores.device)
+    _expect("idx_out", idx_out, (H, min(int(B), L)), torch.int32)
     ws = _workspace(fc_topb_select_workspace_bytes(H, L), scores.device, workspace)
     _check("fc_topb_select", _lib.fc_topb_select(H, L, int(B), _ptr(scores), _ptr(idx_out), _ptr(ws), ws.numel(),
                                                  _stream(stream)))
@@ -298,8 +347,24 @@ class ChunkDecider:
                                 self.workspace, stream)
 
 
+def _expect_chunk_state(p: fc_l1_params, chunk_offsets: Sequence[int], states, per_chunk) -> None:
+    """states: (name, tensor) laid out as the flat chunks; per_chunk: (name,
+    tensor, length, dtype) of the per-chunk (or shared) device arrays."""
+    if len(chunk_offsets) != p.n_chunks + 1:
+        raise ValueError(f"{len(chunk_offsets)} offsets for {p.n_chunks} chunks")
+    need = max(int(x) for x in chunk_offsets)
+    for name, t in states:
+        _expect_flat(name, t, need, _torch_dtype(p.dtype))
+    for name, t, n, dt in per_chunk:
+        _expect(name, t, (n,), dt)
+
+
 def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, step, f, recompute,
                            l1_rel_out=None, workspace=None, stream=None) -> None:
+    n = p.n_chunks
+    _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("X_tm1", X_tm1)),
+                        (("step", step, n, torch.int32), ("f", f, n, torch.float32),
+                         ("recompute", recompute, n, torch.uint8), ("l1_rel_out", l1_rel_out, n, torch.float32)))
     _check("fc_chunk_rel_l1_decide", _lib.fc_chunk_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
         _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -312,6 +377,15 @@ def fc_cache_commit_workspace_bytes(c: fc_cache_params, L_q: int) -> int:
 def fc_cache_commit(c: fc_cache_params, L_clean: int, K_chunk, V_chunk, pos0: int, Q, K_clean, V_clean,
                     pos_clean=None, workspace=None, stream=None) -> int:
     """One commit; returns the new clean length."""
+    H, d, dt = c.H, c.d, _torch_dtype(c.dtype)
+    L_c = int(K_chunk.shape[1])
+    _expect("K_chunk", K_chunk, (H, L_c, d), dt)
+    _expect("V_chunk", V_chunk, (H, L_c, d), dt)
+    _expect("K_clean", K_clean, (H, c.B_budget, d), dt)
+    _expect("V_clean", V_clean, (H, c.B_budget, d), dt)
+    _expect("pos_clean", pos_clean, (H, c.B_budget), torch.int32)
+    if Q is not None:
+        _expect("Q", Q, (H, Q.shape[1], d), dt)
     n = ctypes.c_int32(int(L_clean))
     L_q = int(Q.shape[1]) if Q is not None else 0
     _check("fc_cache_commit", _lib.fc_cache_commit(
@@ -350,6 +424,10 @@ class KvCache:
 
 def fc_euler_step_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, v, dt, X_next, step, f, recompute,
                             l1_rel_out=None, workspace=None, stream=None) -> None:
+    n = p.n_chunks
+    _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("v", v), ("X_next", X_next)),
+                        (("dt", dt, n, torch.float32), ("step", step, n, torch.int32), ("f", f, n, torch.float32),
+                         ("recompute", recompute, n, torch.uint8), ("l1_rel_out", l1_rel_out, n, torch.float32)))
     _check("fc_euler_step_l1_decide", _lib.fc_euler_step_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(v), _ptr(dt), _ptr(X_next), _ptr(step), _ptr(f),
         _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -357,6 +435,11 @@ def fc_euler_step_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, 
 
 def fc_uniform_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, chunk_step, step, f,
                              recompute, l1_rel_out=None, workspace=None, stream=None) -> None:
+    n = p.n_chunks
+    _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("X_tm1", X_tm1)),
+                        (("chunk_step", chunk_step, n, torch.int32), ("step", step, 1, torch.int32),
+                         ("f", f, 1, torch.float32), ("recompute", recompute, n, torch.uint8),
+                         ("l1_rel_out", l1_rel_out, 1, torch.float32)))
     _check("fc_uniform_rel_l1_decide", _lib.fc_uniform_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(chunk_step), _ptr(step), _ptr(f),
         _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -364,6 +447,10 @@ def fc_uniform_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t,
 
 def fc_history_rel_l1_decide(p: fc_l1_params, segment_offsets: Sequence[int], h_prev, h_cur, step, acc, refresh,
                              dev_out=None, workspace=None, stream=None) -> None:
+    n = p.n_chunks
+    _expect_chunk_state(p, segment_offsets, (("h_prev", h_prev), ("h_cur", h_cur)),
+                        (("step", step, n, torch.int32), ("acc", acc, n, torch.float32),
+                         ("refresh", refresh, n, torch.uint8), ("dev_out", dev_out, n, torch.float32)))
     _check("fc_history_rel_l1_decide", _lib.fc_history_rel_l1_decide(
         ctypes.byref(p), _offsets(segment_offsets), _ptr(h_prev), _ptr(h_cur), _ptr(step), _ptr(acc), _ptr(refresh),
         _ptr(dev_out), _ptr(workspace), workspace.numel(), _stream(stream)))

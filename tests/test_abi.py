@@ -174,3 +174,67 @@ def test_cache_argument_errors(fc):
     assert commit(7200, 100, ws_bytes=need // 2) == (fc.FC_ERR_WORKSPACE, 7200)
     assert lib.fc_cache_commit(ctypes.byref(c), None, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, dummy, dummy,
                                need, None) == fc.FC_ERR_INVALID_ARG
+
+
+def test_binding_refuses_mismatched_tensors(fc):
+    # The library trusts the extents its arguments imply; the binding refuses
+    # a tensor of another shape or dtype before any pointer is passed (these
+    # CPU tensors would otherwise only be refused for living on the host).
+    import torch
+    bf = torch.bfloat16
+    Q, K = torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 16, 64, dtype=bf)
+    with pytest.raises(ValueError, match="V: shape"):
+        fc.fc_kv_compress(Q, K, torch.zeros(2, 15, 64, dtype=bf), 4, 0.5, 3)
+    with pytest.raises(ValueError, match="V: dtype"):
+        fc.fc_kv_compress(Q, K, torch.zeros(2, 16, 64), 4, 0.5, 3)
+    with pytest.raises(ValueError, match="K: dtype"):
+        fc.fc_kv_compress(Q, K.float(), K.float(), 4, 0.5, 3)
+    with pytest.raises(ValueError, match="K: shape"):
+        fc.fc_kv_compress(Q, torch.zeros(3, 16, 64, dtype=bf), torch.zeros(3, 16, 64, dtype=bf), 4, 0.5, 3)
+    with pytest.raises(ValueError, match="idx: dtype"):
+        fc.fc_kv_compress(Q, K, K, 4, 0.5, 3, out={"idx": torch.zeros(2, 4, dtype=torch.int64)})
+    with pytest.raises(ValueError, match="K_out: shape"):
+        fc.fc_kv_compress(Q, K, K, 4, 0.5, 3, out={"K_out": torch.zeros(2, 5, 64, dtype=bf)})
+    with pytest.raises(ValueError, match="lse: shape"):
+        fc.fc_kv_importance_colsum(Q, K, torch.zeros(2, 7))
+    with pytest.raises(ValueError, match="r: shape"):
+        fc.fc_kv_select(torch.zeros(2, 16), torch.zeros(2, 15), 4, 0.5, 3)
+    with pytest.raises(ValueError, match="given together"):
+        fc.fc_kv_select(torch.zeros(2, 16), torch.zeros(2, 16), 4, 0.5, 3, K=K)
+    with pytest.raises(ValueError, match="scores: dtype"):
+        fc.fc_topb_select(torch.zeros(2, 16, dtype=torch.float64), 4)
+
+    offs = [0, 100, 250]
+    p = fc.fc_l1_params(2, 1, 0.01, fc.FC_BF16)
+    st, f, rec = torch.zeros(2, dtype=torch.int32), torch.zeros(2), torch.zeros(2, dtype=torch.uint8)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="X_tm1: 249 elements"):
+        fc.fc_chunk_rel_l1_decide(p, offs, torch.zeros(250, dtype=bf), torch.zeros(249, dtype=bf), st, f, rec,
+                                  workspace=ws)
+    with pytest.raises(ValueError, match="X_t: dtype"):
+        fc.fc_chunk_rel_l1_decide(p, offs, torch.zeros(250), torch.zeros(250, dtype=bf), st, f, rec, workspace=ws)
+    with pytest.raises(ValueError, match="step: dtype"):
+        fc.fc_chunk_rel_l1_decide(p, offs, torch.zeros(250, dtype=bf), torch.zeros(250, dtype=bf), st.long(), f,
+                                  rec, workspace=ws)
+    with pytest.raises(ValueError, match="offsets for 2 chunks"):
+        fc.fc_chunk_rel_l1_decide(p, offs[:2], torch.zeros(250, dtype=bf), torch.zeros(250, dtype=bf), st, f, rec,
+                                  workspace=ws)
+    with pytest.raises(ValueError, match="dt: shape"):
+        x = torch.zeros(250, dtype=bf)
+        fc.fc_euler_step_l1_decide(p, offs, x, x, torch.zeros(3), x, st, f, rec, workspace=ws)
+    with pytest.raises(ValueError, match="f: shape"):
+        x = torch.zeros(250, dtype=bf)
+        fc.fc_uniform_rel_l1_decide(p, offs, x, x, st, st[:1], f, rec, workspace=ws)
+
+    c = fc.fc_cache_params(2, 64, 32, 16, 0.5, 3, 0.0, fc.FC_BF16)
+    Kc = torch.zeros(2, 32, 64, dtype=bf)
+    pos = torch.zeros(2, 32, dtype=torch.int32)
+    with pytest.raises(ValueError, match="K_chunk: shape"):
+        fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 128, dtype=bf), torch.zeros(2, 8, 128, dtype=bf), 0, None, Kc,
+                           Kc, pos, ws)
+    with pytest.raises(ValueError, match="pos_clean: dtype"):
+        fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 8, 64, dtype=bf), 0, None, Kc, Kc,
+                           pos.long(), ws)
+    with pytest.raises(ValueError, match="on the GPU"):  # consistent arguments reach the device check
+        fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 8, 64, dtype=bf), 0, None, Kc, Kc,
+                           pos, ws)
