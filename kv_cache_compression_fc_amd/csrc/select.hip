@@ -135,64 +135,61 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
     const bool cached = nch == 1;  // the keys stay in tile_b between the passes
     const int x0 = tid * kKpt;     // this thread's first key in a chunk
 
-    // softmax statistics of r: (max of r*log2e, 1 / sum 2^{r*log2e - max})
-    if constexpr (kFromImp) {
-        if (tid < kWave) {
-            float M = -1e30f, S = 0.f;
-            for (int i = tid; i < nbr; i += kWave) {
-                const float2 v = red_part[(size_t)h * nbr + i];
-                lse2_merge(M, S, v.x, v.y);
-            }
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
-                lse2_merge(M, S, m2, s2);
-            }
-            if (tid == 0) {
-                stat[0] = M;
-                stat[1] = 1.0f / S;
-            }
-        }
-    }
-
     // ---- keys --------------------------------------------------------------------------
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * kChunk;
         const int n = min(kChunk, L - c0);
-        // all loads of the chunk in flight at once, then the LDS stores
-        {
-            const float* rs = (kFromImp ? r : src) + hL + c0;
-            float v[kKpt];
+        // Every load of the chunk is issued before any is waited for: r (or
+        // the scores), then the importance with a halo of hw <= kMaxHalo on
+        // each side (the planes added in a fixed order).
+        constexpr int kQa = (kChunk + 2 * kMaxHalo + kSelThreads - 1) / kSelThreads;
+        const float* rs = (kFromImp ? r : src) + hL + c0;
+        float vr[kKpt], vi[kQa];
 #pragma unroll
-            for (int q = 0; q < kKpt; ++q) {
-                const int i = tid + q * kSelThreads;
-                v[q] = i < n ? rs[i] : 0.f;
-            }
-#pragma unroll
-            for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = __float_as_uint(v[q]);
+        for (int q = 0; q < kKpt; ++q) {
+            const int i = tid + q * kSelThreads;
+            vr[q] = i < n ? rs[i] : 0.f;
         }
         if constexpr (kFromImp) {
-            // importance with a halo of hw <= kMaxHalo on each side (the
-            // planes added in a fixed order)
-            constexpr int kQa = (kChunk + 2 * kMaxHalo + kSelThreads - 1) / kSelThreads;
             const size_t plane = (size_t)gridDim.x * L;
-            float v[kQa];
 #pragma unroll
             for (int q = 0; q < kQa; ++q) {
                 const int i = tid + q * kSelThreads, j = c0 - hw + i;
-                v[q] = (i < kChunk + 2 * hw && j >= 0 && j < L) ? src[hL + j] : -INFINITY;
+                vi[q] = (i < kChunk + 2 * hw && j >= 0 && j < L) ? src[hL + j] : -INFINITY;
             }
             for (int pl = 1; pl < nsrc; ++pl) {
 #pragma unroll
                 for (int q = 0; q < kQa; ++q) {
                     const int i = tid + q * kSelThreads, j = c0 - hw + i;
-                    if (i < kChunk + 2 * hw && j >= 0 && j < L) v[q] += src[pl * plane + hL + j];
+                    if (i < kChunk + 2 * hw && j >= 0 && j < L) vi[q] += src[pl * plane + hL + j];
                 }
             }
+            // softmax statistics of r, (max of r*log2e, 1 / sum 2^{r*log2e - max}),
+            // by wave 0 while the chunk's loads are in flight
+            if (c == 0 && tid < kWave) {
+                float M = -1e30f, S = 0.f;
+                for (int i = tid; i < nbr; i += kWave) {
+                    const float2 v = red_part[(size_t)h * nbr + i];
+                    lse2_merge(M, S, v.x, v.y);
+                }
+#pragma unroll
+                for (int o = kWave / 2; o > 0; o >>= 1) {
+                    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+                    lse2_merge(M, S, m2, s2);
+                }
+                if (tid == 0) {
+                    stat[0] = M;
+                    stat[1] = 1.0f / S;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = __float_as_uint(vr[q]);
+        if constexpr (kFromImp) {
 #pragma unroll
             for (int q = 0; q < kQa; ++q) {
                 const int i = tid + q * kSelThreads;
-                if (i < kChunk + 2 * hw) tile_a[kMaxHalo - hw + i] = v[q];
+                if (i < kChunk + 2 * hw) tile_a[kMaxHalo - hw + i] = vi[q];
             }
         }
         __syncthreads();
@@ -321,27 +318,34 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
         uint32_t kv[kKpt];
         load_keys(c, kv);
         const int j0 = c * kChunk + x0;
-        uint32_t neq = 0;
-#pragma unroll
-        for (int i = 0; i < kKpt; ++i) neq += (j0 + i < L && kv[i] == T);
-        uint32_t tot_eq, tot_sel;
-        uint32_t eq_rank = eq_seen + block_exclusive_scan(neq, scan_lds, &tot_eq);
-        uint32_t sel = 0, nsel = 0;
+        // One scan of both counts (keys > T, keys == T), 16 bits each: a
+        // chunk holds fewer than 2^16 keys.  The equal keys are kept in
+        // token order, the first q of the head, so the keys this thread
+        // keeps land after the greater keys before it and after the kept
+        // equal keys before it.
+        uint32_t ngt = 0, neq = 0;
 #pragma unroll
         for (int i = 0; i < kKpt; ++i) {
-            bool s = false;
-            if (j0 + i < L) {
-                if (kv[i] > T) s = true;
-                else if (kv[i] == T) { s = eq_rank < q; ++eq_rank; }
-            }
-            if (s) { sel |= 1u << i; ++nsel; }
+            ngt += (j0 + i < L && kv[i] > T);
+            neq += (j0 + i < L && kv[i] == T);
         }
+        uint32_t tot;
+        const uint32_t before = block_exclusive_scan(ngt | (neq << 16), scan_lds, &tot);
+        const uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
+        const uint32_t tot_gt = tot & 0xffffu, tot_eq = tot >> 16;
+        const uint32_t eq_kept_before = min(eq_seen + eq_before, q) - min(eq_seen, q);
+        const uint32_t tot_sel = tot_gt + min(eq_seen + tot_eq, q) - min(eq_seen, q);
+        uint32_t eq_rank = eq_seen + eq_before;
         // kept indices go to their slots of this chunk's output in area A,
         // then out with coalesced stores
-        uint32_t pos = block_exclusive_scan(nsel, scan_lds, &tot_sel);
+        uint32_t pos = gt_before + eq_kept_before;
 #pragma unroll
         for (int i = 0; i < kKpt; ++i) {
-            if (sel & (1u << i)) area_a[pos++] = (uint32_t)(j0 + i);
+            if (j0 + i < L) {
+                bool s = kv[i] > T;
+                if (kv[i] == T) { s = eq_rank < q; ++eq_rank; }
+                if (s) area_a[pos++] = (uint32_t)(j0 + i);
+            }
         }
         __syncthreads();
         for (uint32_t i = tid; i < tot_sel; i += kSelThreads)
