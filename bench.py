@@ -328,6 +328,23 @@ def main() -> int:
     t_compress = time_events(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws),
                              reps)
     t_l1 = time_events(lambda: dec.decide(xt_d, xtm1_d), reps)
+    # the other two decision rules on the same pair of states: one decision
+    # for all chunks (uniform), and the history-guided refresh per chunk
+    n_ch = ccfg.n_chunks
+    offs_c = [i * ccfg.chunk_elems for i in range(n_ch + 1)]
+    p_pol = fc.fc_l1_params(n_ch, ccfg.m, ccfg.eps[0], fc.FC_BF16)
+    ws_pol = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p_pol, offs_c), dtype=torch.uint8, device=dev)
+    cstep = torch.tensor(steps, dtype=torch.int32, device=dev)
+    gstep = torch.zeros(1, dtype=torch.int32, device=dev)
+    f_u, l1_u = torch.zeros(1, device=dev), torch.zeros(1, device=dev)
+    rec_u = torch.zeros(n_ch, dtype=torch.uint8, device=dev)
+    t_uni = time_events(lambda: fc.fc_uniform_rel_l1_decide(p_pol, offs_c, xt_d, xtm1_d, cstep, gstep, f_u, rec_u,
+                                                            l1_u, ws_pol), reps)
+    hstep = torch.tensor(steps, dtype=torch.int32, device=dev)
+    acc_h, dev_h = torch.zeros(n_ch, device=dev), torch.zeros(n_ch, device=dev)
+    ref_h = torch.zeros(n_ch, dtype=torch.uint8, device=dev)
+    t_hist = time_events(lambda: fc.fc_history_rel_l1_decide(p_pol, offs_c, xt_d, xtm1_d, hstep, acc_h, ref_h,
+                                                             dev_h, ws_pol), reps)
     # the HBM-bound stages again with the MALL flushed before every call
     scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB
     t_red_c, _ = time_cold(lambda: fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws), reps, scratch)
@@ -360,6 +377,8 @@ def main() -> int:
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "euler_l1_fused_ms": t_fused, "euler_l1_fused_gbps": fused_bytes / (t_fused * 1e-3) / 1e9,
+        "uniform_l1_ms": t_uni, "uniform_l1_gbps": l1_bytes / (t_uni * 1e-3) / 1e9,
+        "history_l1_ms": t_hist, "history_l1_gbps": l1_bytes / (t_hist * 1e-3) / 1e9,
         "mall_flushed": {
             "redundancy_standalone_ms": t_red_c, "redundancy_standalone_gbps": red_bytes / (t_red_c * 1e-3) / 1e9,
             "select_gather_ms": t_sel_c, "select_gather_gbps": sel_bytes / (t_sel_c * 1e-3) / 1e9,
