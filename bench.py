@@ -373,6 +373,8 @@ def main() -> int:
     stages = {
         "importance_lse_ms": t_lse, "importance_lse_tflops": lse_tflops,
         "importance_colsum_ms": t_colsum, "importance_colsum_tflops": mfma_flops / (t_colsum * 1e-3) / 1e12,
+        # Q K^T counted once over both passes (the two-pass method executes it twice)
+        "importance_algorithmic_tflops": mfma_flops / ((t_lse + t_colsum) * 1e-3) / 1e12,
         "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
