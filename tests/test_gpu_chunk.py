@@ -101,8 +101,9 @@ def test_unaligned_offsets_and_edge_chunks(fc):
 def test_inactive_chunks_untouched(fc):
     n, e = 6, 5000
     offs = [i * e for i in range(n + 1)]
-    x = torch.randn(n * e, dtype=torch.float32)
-    y = x + 0.001 * torch.randn(n * e)
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn(n * e, dtype=torch.float32, generator=g)
+    y = x + 0.001 * torch.randn(n * e, generator=g)
     dec = fc.ChunkDecider(offs, 1, 0.01, torch.float32, DEV)
     dec.step.copy_(torch.tensor([-1, 0, -5, 3, -1, 2], dtype=torch.int32))
     dec.f.copy_(torch.tensor([7.0, 0.0, 8.0, 0.001, 9.0, 0.0]))
@@ -123,7 +124,7 @@ def test_repeated_calls_share_workspace(fc):
     # the same workspace over many calls
     n, e = 3, 200000
     offs = [i * e for i in range(n + 1)]
-    x = torch.randn(n * e).to(torch.bfloat16)
+    x = torch.randn(n * e, generator=torch.Generator().manual_seed(22)).to(torch.bfloat16)
     y = (x.float() * 1.01).to(torch.bfloat16)
     dec = fc.ChunkDecider(offs, 0, 1.0, torch.bfloat16, DEV)
     dec.step.zero_()

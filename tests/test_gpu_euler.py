@@ -121,8 +121,10 @@ def test_rounding_cases_in_head_tail_and_body(fc):
 def test_inactive_chunks_untouched(fc):
     say("case: fused update leaves inactive chunks unread and unwritten")
     offs = [0, 1000, 2500, 2501, 4000]
-    x = torch.randn(4000, device=DEV).to(torch.bfloat16)
-    v = torch.randn(4000, device=DEV).to(torch.bfloat16)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(23)
+    x = torch.randn(4000, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(4000, generator=g, device=DEV).to(torch.bfloat16)
     y = torch.full((4000,), 3.0, dtype=torch.bfloat16, device=DEV)
     dec = fc.ChunkDecider(offs, 0, 0.1, torch.bfloat16, DEV)
     dec.step.copy_(torch.tensor([0, -1, 5, -1], dtype=torch.int32))

@@ -148,8 +148,10 @@ def test_edge_chunks_and_inactive_steps(fc):
     # +inf), and a step with every chunk inactive, under both rules
     say("case: uniform and history rules on zero-length, zero-norm and inactive chunks")
     offs = [0, 0, 1000, 1000, 3000, 3001]
-    x = torch.randn(3001, device=DEV).to(torch.bfloat16)
-    y = torch.randn(3001, device=DEV).to(torch.bfloat16)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    x = torch.randn(3001, generator=g, device=DEV).to(torch.bfloat16)
+    y = torch.randn(3001, generator=g, device=DEV).to(torch.bfloat16)
     x[1000:3000] = 0
     p = fc.fc_l1_params(5, 1, 0.3, fc.FC_BF16)
     ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, offs), dtype=torch.uint8, device=DEV)
@@ -168,7 +170,9 @@ def test_edge_chunks_and_inactive_steps(fc):
         if np.isinf(want[i]):
             assert np.isinf(got[i]) and np.isinf(acc.cpu()[i].item())
         else:
-            assert abs(got[i] - want[i]) <= 1e-5 * want[i] and abs(acc.cpu()[i].item() - a) <= 1e-6
+            # acc is float32: its rounding is relative (the one-element
+            # segment's ratio can be far above 1)
+            assert abs(got[i] - want[i]) <= 1e-5 * want[i] and abs(acc.cpu()[i].item() - a) <= 1e-6 * max(1.0, a)
     # uniform rule with every chunk inactive: nothing read, flags untouched,
     # L1 over no elements is +inf, so the step recomputes
     cstep = torch.full((5,), -1, dtype=torch.int32, device=DEV)
