@@ -775,9 +775,17 @@ ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d) {
     choose_split((long long)H * ((Lq + kRowsPerBlock - 1) / kRowsPerBlock), (Lk + kt - 1) / kt, 4, 1 << 20,
                  sl.lse, &p.nsplit, &kps_tiles);
     p.keys_per_split = kps_tiles * kt;
-    // pass 2: query ranges of whole Q tiles (>= 4 tiles each, at most kMaxQSplit)
-    choose_split((long long)H * ((Lk + kRowsPerBlock - 1) / kRowsPerBlock), (Lq + kt - 1) / kt, 4, kMaxQSplit,
-                 sl.colsum, &p.nqs, &p.qtiles_per_split);
+    // pass 2: one range of queries per key block when the key blocks alone
+    // fill the device's workgroup slots; otherwise just enough query ranges
+    // (whole Q tiles, >= 4 each, at most kMaxQSplit) to fill them
+    const long long groups = (long long)H * ((Lk + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int qtiles = (Lq + kt - 1) / kt;
+    long long parts = groups >= sl.colsum ? 1 : sl.colsum / groups;
+    if (parts > qtiles / 4) parts = qtiles / 4;
+    if (parts > kMaxQSplit) parts = kMaxQSplit;
+    if (parts < 1) parts = 1;
+    p.qtiles_per_split = (int)((qtiles + parts - 1) / parts);
+    p.nqs = (qtiles + p.qtiles_per_split - 1) / p.qtiles_per_split;  // every range non-empty
     return p;
 }
 

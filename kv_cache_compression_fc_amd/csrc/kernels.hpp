@@ -11,11 +11,13 @@ namespace fc {
 // Pass 1 splits the keys of each head into `nsplit` ranges of
 // `keys_per_split` keys (whole key tiles), chosen from the device's
 // workgroup slots so that the last round of the grid is nearly full.  Pass 2
-// can split the queries into `nqs` ranges of `qtiles_per_split` query tiles,
-// one partial importance plane per range; measured on the MAGI-like shape,
-// every split costs more in per-workgroup set-up (each range re-loads its
-// keys) than it saves in the grid's last round, so the limit is one range.
-constexpr int kMaxQSplit = 1;
+// splits the queries into `nqs` ranges of `qtiles_per_split` query tiles,
+// one partial importance plane per range, only when its key blocks alone
+// leave workgroup slots idle (few keys, many queries): measured on the
+// MAGI-like shape, where the key blocks fill several rounds, any split costs
+// more in per-workgroup set-up (each range re-loads its keys) than it saves
+// in the grid's last round.
+constexpr int kMaxQSplit = 64;
 struct ImpPlan {
     int nsplit;
     int keys_per_split;

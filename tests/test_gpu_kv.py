@@ -80,6 +80,10 @@ RAGGED = [
     ("f32", 64, 2, 37, 333, 100, 5),
     ("f32", 128, 1, 70, 190, 50, 1),
     ("bf16", 64, 5, 31, 65, 64, 9),
+    # few key blocks, many queries: pass 2 splits the queries into ranges
+    # (partial importance planes added by the select)
+    ("bf16", 128, 2, 2000, 700, 300, 7),
+    ("f32", 64, 1, 1000, 300, 100, 5),
 ]
 
 
@@ -128,9 +132,11 @@ def test_zero_and_duplicate_keys(fc):
     assert torch.isfinite(out["score"]).all()
 
 
-def test_importance_stage(fc):
-    Q, K, _ = synth.random_kv(3, 300, 1000, 128, "bf16", seed=9)
-    say("case: fc_kv_importance bf16 H=3 Lq=300 Lk=1000")
+@pytest.mark.parametrize("H,Lq,Lk", [(3, 300, 1000), (2, 2500, 500)])
+def test_importance_stage(fc, H, Lq, Lk):
+    # the second shape splits pass 2 into query ranges (planes added after)
+    Q, K, _ = synth.random_kv(H, Lq, Lk, 128, "bf16", seed=9)
+    say(f"case: fc_kv_importance bf16 H={H} Lq={Lq} Lk={Lk}")
     imp = fc.fc_kv_importance(Q.to(DEV), K.to(DEV))
     torch.cuda.synchronize()
     want = oracle.importance(Q, K, 1 / math.sqrt(128))
@@ -188,7 +194,8 @@ def test_deterministic(fc):
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("dtype,d,H,Lq,Lk", [("bf16", 128, 3, 200, 3000), ("f32", 64, 2, 65, 513)])
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk", [("bf16", 128, 3, 200, 3000), ("f32", 64, 2, 65, 513),
+                                             ("bf16", 64, 1, 3000, 400)])
 def test_importance_two_stages(fc, dtype, d, H, Lq, Lk):
     # pass 1 (lse) against the oracle's log-sum-exp, then pass 2 fed with it
     Q, K, _ = synth.random_kv(H, Lq, Lk, d, dtype, seed=12)
