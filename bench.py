@@ -140,8 +140,14 @@ def cpu_baseline(cfg, ccfg, min_seconds: float):
                 _, f[i] = oracle.decide(n, f[i], l1[i], ccfg.m, ccfg.eps[0])
         t_total += time.perf_counter() - t0
         reps += 1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": cfg.H * cfg.Lk * reps / t_total, "unit": "token-heads/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": t_total,
+            "cpu": cpu, "kind": "oracle", "seconds": t_total,
             "sample": f"{reps} whole step(s) of the same workload: fp64 compression of all {cfg.H} heads "
                       f"(L_q={cfg.Lq}, L_k={cfg.Lk}, C + OpenMP importance, numpy rest) and the relative-L1 "
                       f"decision of {ccfg.n_chunks} chunks (numpy)"}
