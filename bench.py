@@ -239,6 +239,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache", action="store_true",
                     help="skip the KV-cache run and the SkyReels-like / long-video compressions")
+    ap.add_argument("--loop-lse", type=float, default=0.0, metavar="SECONDS",
+                    help="only run importance pass 1 on the MAGI-like shape back to back for SECONDS "
+                         "(to read the board's power and clocks meanwhile)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
     args = ap.parse_args()
@@ -268,6 +271,21 @@ def main() -> int:
 
     cfg = synth.KV_CONFIGS["magi"]
     ccfg = synth.CHUNK_CONFIGS["scale"]
+    if args.loop_lse > 0:
+        Q, K, _ = synth.kv_inputs(cfg, seed=0)
+        Qd, Kd = Q.to(dev), K.to(dev)
+        lse = fc.fc_kv_importance_lse(Qd, Kd)
+        torch.cuda.synchronize()
+        log("loop start")
+        t0, calls = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.loop_lse:
+            for _ in range(50):
+                fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse)
+            torch.cuda.synchronize()
+            calls += 50
+        dt = time.perf_counter() - t0
+        print(json.dumps({"loop_lse_calls": calls, "ms_per_call": 1e3 * dt / calls}), flush=True)
+        return 0
     log(f"generating inputs: {cfg.name} KV workload and {ccfg.n_chunks} chunk states")
     Q, K, V = synth.kv_inputs(cfg, seed=0)
     Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
