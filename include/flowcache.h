@@ -105,7 +105,8 @@ size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
  *                                                     redundancy softmax
  *   workspace                                         device, >= the query
  * Selection order: larger score first; equal scores keep the lower index.
- * L_k <= B_budget keeps every token (idx = 0..L_k-1).  Zero-norm keys are
+ * L_k <= B_budget keeps every token (idx = 0..L_k-1); when no score output
+ * is asked for, that call only copies the rows.  Zero-norm keys are
  * normalised with max(||k||, 1e-12) and so contribute no similarity.
  * Deterministic: identical inputs give bit-identical outputs.
  */

@@ -119,6 +119,11 @@ fc_status kv_compress_run(const fc_kv_params* p, const KvLayout& L, const void* 
                           int32_t* pos_out = nullptr) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
+    if (Bp == p->L_k && !score_out && !imp_pooled_out && !red_out) {
+        // every token is kept and no score is asked for: the rows are copied
+        FC_TRY(launch_gather(dt, p->d, nullptr, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out, idx_out));
+        return FC_OK;
+    }
     float* imp = at<float>(ws, L.imp);
     float* r = at<float>(ws, L.r);
     float2* red_part = at<float2>(ws, L.red_part);

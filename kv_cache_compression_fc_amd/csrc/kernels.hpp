@@ -79,10 +79,12 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
                            int L, int Bp, int32_t* idx_out, hipStream_t s);
 // K_out[h][b] = K[h][idx[h][b]], V likewise; with pos_out also
-// pos_out[h][b] = pos[h][idx[h][b]] (pos [H][L], pos_out [H][Bp]).
+// pos_out[h][b] = pos[h][idx[h][b]] (pos [H][L], pos_out [H][Bp]).  With
+// idx_keep_all (Bp == L) every row is kept: idx is not read, and
+// idx_keep_all[h][b] = b is written.
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
                          void* K_out, void* V_out, hipStream_t s, const int32_t* pos = nullptr,
-                         int32_t* pos_out = nullptr);
+                         int32_t* pos_out = nullptr, int32_t* idx_keep_all = nullptr);
 
 // ---- KV cache manager -----------------------------------------------------------
 // dst[h][row0 + j] = j < n_old ? old[h][j] : fresh[h][j - n_old] for K and V,

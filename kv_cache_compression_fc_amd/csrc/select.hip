@@ -363,8 +363,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
 constexpr int kThreads = 256;
 constexpr int kGatherRows = 32;  // measured 62.6 -> 60.0 us for select + gather (MAGI-like) against 64
 
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __restrict__ idx, int L, int Bp,
+// kKeepAll: every row is kept (B' = L): the kernel writes idx[h][b] = b
+// itself instead of reading it.
+template <int DT, int D, bool kKeepAll>
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(int32_t* __restrict__ idx, int L, int Bp,
                                                                const void* __restrict__ K, const void* __restrict__ V,
                                                                void* __restrict__ K_out, void* __restrict__ V_out,
                                                                const int32_t* __restrict__ pos,
@@ -384,7 +386,12 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
         const int b = b0 + i * kRpi;
-        j[i] = b < Bp ? idx[(size_t)h * Bp + b] : -1;
+        if constexpr (kKeepAll) {
+            j[i] = b < Bp ? b : -1;
+            if (b < Bp && e == 0) idx[(size_t)h * Bp + b] = b;
+        } else {
+            j[i] = b < Bp ? idx[(size_t)h * Bp + b] : -1;
+        }
     }
     uint4 kv[kSteps], vv[kSteps];
 #pragma unroll
@@ -407,10 +414,14 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const int32_t* __
 
 template <int DT, int D>
 hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
-                         void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s) {
+                         void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s, int32_t* idx_keep_all) {
     const dim3 grid((Bp + kGatherRows - 1) / kGatherRows, H);
-    hipLaunchKernelGGL((gather_rows_kernel<DT, D>), grid, dim3(kThreads), 0, s, idx, L, Bp, K, V, K_out, V_out, pos,
-                       pos_out);
+    if (idx_keep_all != nullptr)
+        hipLaunchKernelGGL((gather_rows_kernel<DT, D, true>), grid, dim3(kThreads), 0, s, idx_keep_all, L, Bp, K, V,
+                           K_out, V_out, pos, pos_out);
+    else
+        hipLaunchKernelGGL((gather_rows_kernel<DT, D, false>), grid, dim3(kThreads), 0, s, const_cast<int32_t*>(idx),
+                           L, Bp, K, V, K_out, V_out, pos, pos_out);
     return hipGetLastError();
 }
 
@@ -429,12 +440,13 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
 }
 
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
-                         void* K_out, void* V_out, hipStream_t s, const int32_t* pos, int32_t* pos_out) {
+                         void* K_out, void* V_out, hipStream_t s, const int32_t* pos, int32_t* pos_out,
+                         int32_t* idx_keep_all) {
     if (dt == kBF16)
-        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s)
-                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s);
-    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s)
-                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s);
+        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all)
+                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all);
+    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all)
+                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all);
 }
 
 }  // namespace fc

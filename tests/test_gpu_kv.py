@@ -105,10 +105,19 @@ def test_explicit_scale_and_lambda_extremes(fc):
 def test_budget_covers_all_tokens(fc):
     Q, K, V = synth.random_kv(2, 40, 90, 128, "bf16", seed=5)
     for B in (90, 500):
-        say(f"case: B={B} >= Lk=90 keeps every token")
-        out = gpu_compress(fc, Q, K, V, B, 0.5, 7)
-        assert torch.equal(out["idx"].cpu(), torch.arange(90, dtype=torch.int32).repeat(2, 1))
-        assert torch.equal(out["K_out"].cpu(), K) and torch.equal(out["V_out"].cpu(), V)
+        for scores in (True, False):  # without score outputs the call only copies the rows
+            say(f"case: B={B} >= Lk=90 keeps every token (score outputs: {scores})")
+            out = fc.fc_kv_compress(Q.to(DEV), K.to(DEV), V.to(DEV), B, 0.5, 7, want_scores=scores)
+            torch.cuda.synchronize()
+            assert torch.equal(out["idx"].cpu(), torch.arange(90, dtype=torch.int32).repeat(2, 1))
+            assert torch.equal(out["K_out"].cpu(), K) and torch.equal(out["V_out"].cpu(), V)
+    # larger, fp32, ragged: rows past several gather blocks
+    Q, K, V = synth.random_kv(3, 5, 1001, 64, "f32", seed=6)
+    say("case: B=1001 = Lk, f32 d=64, no score outputs")
+    out = fc.fc_kv_compress(Q.to(DEV), K.to(DEV), V.to(DEV), 1001, 0.5, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(out["idx"].cpu(), torch.arange(1001, dtype=torch.int32).repeat(3, 1))
+    assert torch.equal(out["K_out"].cpu(), K) and torch.equal(out["V_out"].cpu(), V)
 
 
 def test_single_key_and_single_budget(fc):
