@@ -28,8 +28,7 @@ Video Generation" (papernotes.org ICLR 2026 digest), section 方法详解 /
   merged into the clean tokens and, when they no longer fit, compressed back
   to B_budget.
 
-Readings where the page leaves a step open (each is also listed in the design
-notes of the repository):
+Readings where the page leaves a step open:
 
 * softmax temperature: the usual attention scale 1/sqrt(d) unless a scale is
   given;                                                    (parity unpinned)
