@@ -107,7 +107,9 @@ size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
  * Selection order: larger score first; equal scores keep the lower index.
  * L_k <= B_budget keeps every token (idx = 0..L_k-1); when no score output
  * is asked for, that call only copies the rows.  Zero-norm keys are
- * normalised with max(||k||, 1e-12) and so contribute no similarity.
+ * normalised with max(||k||, 1e-12) and so contribute no similarity.  A
+ * key's squared norm is summed in float32: keys whose squared norm exceeds
+ * the float32 range (elements beyond about 1e19) are outside the domain.
  * Deterministic: identical inputs give bit-identical outputs.
  */
 fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, const void* V,
