@@ -37,6 +37,9 @@ constexpr int kChunk = kSelThreads * kKpt;    // 18432 keys per chunk
 constexpr int kMaxHalo = 64;                  // pool half-window limit ((w-1)/2 <= 64)
 constexpr int kRegHalo = 4;                   // half-windows served from registers
 constexpr int kAWords = kMaxHalo + kChunk + kMaxHalo;  // LDS area A: importance tile / histograms / staging
+constexpr int kR4 = (kChunk / 4 + kSelThreads - 1) / kSelThreads;    // 4-key groups of a chunk per thread
+constexpr int kA4 = (kAWords / 4 + kSelThreads - 1) / kSelThreads;   // 4-key groups of area A per thread
+static_assert(kMaxHalo % 4 == 0 && kChunk % 4 == 0, "4-key groups align with the chunk and its halo");
 
 // Larger float -> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -112,7 +115,7 @@ __device__ __forceinline__ uint32_t find_bin_from_top(const uint32_t* hist, uint
 // kFromImp: scores from importance (nsrc planes [nsrc][H][L] that add up to
 // it; pooled here) and redundancy r with its softmax partials red_part
 // [H][nbr]; otherwise `src` holds the scores.
-template <bool kFromImp>
+template <bool kFromImp, bool kVec>
 __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
     const float* __restrict__ src, int nsrc, const float* __restrict__ r, const float2* __restrict__ red_part, int nbr,
     float lam, int hw, float* __restrict__ score_out, float* __restrict__ imp_pooled_out,
@@ -135,6 +138,27 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
     const bool cached = nch == 1;  // the keys stay in tile_b between the passes
     const int x0 = tid * kKpt;     // this thread's first key in a chunk
 
+    // softmax statistics of r, (max of r*log2e, 1 / sum 2^{r*log2e - max}),
+    // by wave 0 while the first chunk's loads are in flight
+    auto red_stats = [&]() {
+        if (tid < kWave) {
+            float M = -1e30f, S = 0.f;
+            for (int i = tid; i < nbr; i += kWave) {
+                const float2 v = red_part[(size_t)h * nbr + i];
+                lse2_merge(M, S, v.x, v.y);
+            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+                lse2_merge(M, S, m2, s2);
+            }
+            if (tid == 0) {
+                stat[0] = M;
+                stat[1] = 1.0f / S;
+            }
+        }
+    };
+
     // ---- keys --------------------------------------------------------------------------
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * kChunk;
@@ -144,6 +168,62 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
         // each side (the planes added in a fixed order).
         constexpr int kQa = (kChunk + 2 * kMaxHalo + kSelThreads - 1) / kSelThreads;
         const float* rs = (kFromImp ? r : src) + hL + c0;
+        const size_t plane = (size_t)gridDim.x * L;
+        if constexpr (kVec) {
+            // 16-byte loads: r (or the scores) as 4-key groups of the chunk,
+            // the importance as 4-key groups of [c0 - kMaxHalo, c0 + kChunk +
+            // kMaxHalo) (keys outside [0, L) read as -inf), each group
+            // stored at its own place in LDS
+            float4 vr4[kR4], vi4[kA4];
+#pragma unroll
+            for (int q = 0; q < kR4; ++q) {
+                const int g = tid + q * kSelThreads, e = 4 * g;
+                if (e + 3 < n) {
+                    vr4[q] = *reinterpret_cast<const float4*>(rs + e);
+                } else {
+                    vr4[q].x = e < n ? rs[e] : 0.f;
+                    vr4[q].y = e + 1 < n ? rs[e + 1] : 0.f;
+                    vr4[q].z = e + 2 < n ? rs[e + 2] : 0.f;
+                    vr4[q].w = e + 3 < n ? rs[e + 3] : 0.f;
+                }
+            }
+            if constexpr (kFromImp) {
+                for (int pl = 0; pl < nsrc; ++pl) {
+                    const float* ps = src + pl * plane + hL;
+#pragma unroll
+                    for (int q = 0; q < kA4; ++q) {
+                        const int g = tid + q * kSelThreads, j = c0 - kMaxHalo + 4 * g;
+                        float4 x;
+                        if (j >= 0 && j + 3 < L) {
+                            x = *reinterpret_cast<const float4*>(ps + j);
+                        } else {
+                            x.x = (j >= 0 && j < L) ? ps[j] : -INFINITY;
+                            x.y = (j + 1 >= 0 && j + 1 < L) ? ps[j + 1] : -INFINITY;
+                            x.z = (j + 2 >= 0 && j + 2 < L) ? ps[j + 2] : -INFINITY;
+                            x.w = (j + 3 >= 0 && j + 3 < L) ? ps[j + 3] : -INFINITY;
+                        }
+                        if (pl == 0) vi4[q] = x;
+                        else { vi4[q].x += x.x; vi4[q].y += x.y; vi4[q].z += x.z; vi4[q].w += x.w; }
+                    }
+                }
+            }
+            if (c == 0 && kFromImp) red_stats();
+#pragma unroll
+            for (int q = 0; q < kR4; ++q) {
+                const int g = tid + q * kSelThreads;
+                if (4 * g < kChunk)
+                    reinterpret_cast<uint4*>(tile_b)[g] = make_uint4(__float_as_uint(vr4[q].x), __float_as_uint(vr4[q].y),
+                                                                     __float_as_uint(vr4[q].z), __float_as_uint(vr4[q].w));
+            }
+            if constexpr (kFromImp) {
+#pragma unroll
+                for (int q = 0; q < kA4; ++q) {
+                    const int g = tid + q * kSelThreads;
+                    if (4 * g < kAWords) reinterpret_cast<float4*>(tile_a)[g] = vi4[q];
+                }
+            }
+            __syncthreads();
+        } else {
         float vr[kKpt], vi[kQa];
 #pragma unroll
         for (int q = 0; q < kKpt; ++q) {
@@ -151,7 +231,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
             vr[q] = i < n ? rs[i] : 0.f;
         }
         if constexpr (kFromImp) {
-            const size_t plane = (size_t)gridDim.x * L;
 #pragma unroll
             for (int q = 0; q < kQa; ++q) {
                 const int i = tid + q * kSelThreads, j = c0 - hw + i;
@@ -164,24 +243,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
                     if (i < kChunk + 2 * hw && j >= 0 && j < L) vi[q] += src[pl * plane + hL + j];
                 }
             }
-            // softmax statistics of r, (max of r*log2e, 1 / sum 2^{r*log2e - max}),
-            // by wave 0 while the chunk's loads are in flight
-            if (c == 0 && tid < kWave) {
-                float M = -1e30f, S = 0.f;
-                for (int i = tid; i < nbr; i += kWave) {
-                    const float2 v = red_part[(size_t)h * nbr + i];
-                    lse2_merge(M, S, v.x, v.y);
-                }
-#pragma unroll
-                for (int o = kWave / 2; o > 0; o >>= 1) {
-                    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
-                    lse2_merge(M, S, m2, s2);
-                }
-                if (tid == 0) {
-                    stat[0] = M;
-                    stat[1] = 1.0f / S;
-                }
-            }
+            if (c == 0) red_stats();
         }
 #pragma unroll
         for (int q = 0; q < kKpt; ++q) tile_b[tid + q * kSelThreads] = __float_as_uint(vr[q]);
@@ -193,6 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
             }
         }
         __syncthreads();
+        }
         const float M = kFromImp ? stat[0] : 0.f, invS = kFromImp ? stat[1] : 0.f;
         float pooled[kKpt];
         if constexpr (kFromImp) {
@@ -430,12 +493,19 @@ hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K
 hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
                            int L, int Bp, int32_t* idx_out, hipStream_t s) {
-    if (r != nullptr)
-        hipLaunchKernelGGL(sel_head_kernel<true>, dim3(H), dim3(kSelThreads), 0, s, src, nsrc, r, red_part, nbr, lam,
-                           (w - 1) / 2, score_out, imp_pooled_out, red_out, keys, L, Bp, idx_out);
-    else
-        hipLaunchKernelGGL(sel_head_kernel<false>, dim3(H), dim3(kSelThreads), 0, s, src, 1, nullptr, nullptr, 0,
-                           0.f, 0, nullptr, nullptr, nullptr, keys, L, Bp, idx_out);
+    // 16-byte loads when every head's rows of every input start 16-byte
+    // aligned: L a multiple of 4 and aligned bases
+    const bool vec = L % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                     (r == nullptr || (reinterpret_cast<uintptr_t>(r) & 15) == 0);
+    if (r != nullptr) {
+        auto kern = vec ? sel_head_kernel<true, true> : sel_head_kernel<true, false>;
+        hipLaunchKernelGGL(kern, dim3(H), dim3(kSelThreads), 0, s, src, nsrc, r, red_part, nbr, lam, (w - 1) / 2,
+                           score_out, imp_pooled_out, red_out, keys, L, Bp, idx_out);
+    } else {
+        auto kern = vec ? sel_head_kernel<false, true> : sel_head_kernel<false, false>;
+        hipLaunchKernelGGL(kern, dim3(H), dim3(kSelThreads), 0, s, src, 1, nullptr, nullptr, 0, 0.f, 0, nullptr,
+                           nullptr, nullptr, keys, L, Bp, idx_out);
+    }
     return hipGetLastError();
 }
 
