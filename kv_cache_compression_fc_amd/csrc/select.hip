@@ -493,9 +493,12 @@ hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K
 hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
                            int L, int Bp, int32_t* idx_out, hipStream_t s) {
-    // 16-byte loads when every head's rows of every input start 16-byte
-    // aligned: L a multiple of 4 and aligned bases
-    const bool vec = L % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+    // 16-byte loads when a head fits one chunk and every head's rows of
+    // every input start 16-byte aligned (L a multiple of 4, aligned bases).
+    // Heads of several chunks keep the 4-byte loads: measured on the
+    // long-video shape, the 16-byte form was slower there (171.0 against
+    // 166.5 us), against 27.0 -> 26.0 us on the MAGI-like shape.
+    const bool vec = L <= kChunk && L % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
                      (r == nullptr || (reinterpret_cast<uintptr_t>(r) & 15) == 0);
     if (r != nullptr) {
         auto kern = vec ? sel_head_kernel<true, true> : sel_head_kernel<true, false>;
