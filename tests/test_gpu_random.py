@@ -1,0 +1,115 @@
+"""Seeded random sweeps through the C ABI against the fp64 oracle: small
+compressions over every dtype, head size, window, lambda and temperature
+the boundary accepts (with one-query, one-key and budget-above-L_k corners),
+and chunk decisions over random, unaligned chunk tables with random states,
+step counters and accumulators.  The configurations come from fixed seeds,
+so every run draws the same ones."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from kv_cache_compression_fc_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from kv_cache_compression_fc_amd import binding
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def kv_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = ("bf16", "f32")[int(rng.integers(2))]
+        d = (64, 128)[int(rng.integers(2))]
+        H = int(rng.integers(1, 5))
+        Lq = 1 if rng.uniform() < 0.15 else int(rng.integers(2, 400))
+        Lk = 1 if rng.uniform() < 0.1 else int(rng.integers(2, 3000))
+        B = int(rng.integers(1, Lk + 10))
+        w = int(rng.choice([1, 3, 5, 7, 9]))
+        u = rng.uniform()
+        lam = 0.0 if u < 0.15 else (1.0 if u < 0.3 else round(float(rng.uniform()), 3))
+        scale = 0.0 if rng.uniform() < 0.5 else round(float(rng.uniform(0.02, 0.3)), 4)
+        out.append((dtype, d, H, Lq, Lk, B, w, lam, scale, 1000 + i))
+    return out
+
+
+CORNERS = [
+    # one query and one key; one key, budget above it; every token kept with
+    # lambda = 1; lambda = 0 with a wide window; a 1-wide window at B = 1
+    ("bf16", 128, 2, 1, 1, 1, 1, 1.0, 0.0, 901),
+    ("f32", 64, 3, 50, 1, 5, 3, 0.5, 0.0, 902),
+    ("bf16", 128, 1, 300, 500, 600, 7, 1.0, 0.0, 903),
+    ("bf16", 64, 2, 129, 777, 100, 9, 0.0, 0.2, 904),
+    ("f32", 128, 2, 64, 1000, 1, 1, 0.5, 0.0, 905),
+]
+
+
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk,B,w,lam,scale,seed", kv_configs(16, 2026) + CORNERS)
+def test_random_compress(fc, dtype, d, H, Lq, Lk, B, w, lam, scale, seed):
+    say(f"case: {dtype} d={d} H={H} Lq={Lq} Lk={Lk} B={B} w={w} lambda={lam} scale={scale} seed={seed}")
+    Q, K, V = synth.random_kv(H, Lq, Lk, d, dtype, seed=seed)
+    out = fc.fc_kv_compress(Q.to(DEV), K.to(DEV), V.to(DEV), B, lam, w, scale, want_scores=True)
+    torch.cuda.synchronize()
+    ref = oracle.kv_compress(Q, K, V, B, lam, w, None if scale == 0.0 else scale)
+    parity.check_scores(out, ref, lam)
+    parity.check_selection(out["idx"], ref["score"], B)
+    parity.check_gather(K.to(DEV), V.to(DEV), out["idx"], out["K_out"], out["V_out"])
+    parity.check_selection_consistent(out["idx"], out["score"], B)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_chunk_decisions(fc, seed):
+    rng = np.random.default_rng(3000 + seed)
+    n = int(rng.integers(1, 12))
+    sizes = [0 if rng.uniform() < 0.15 else int(rng.integers(1, 50000)) for _ in range(n)]
+    offs = [int(rng.integers(0, 9))]
+    for s in sizes:
+        offs.append(offs[-1] + s)
+    total = offs[-1] + int(rng.integers(0, 9))
+    dtype = (torch.bfloat16, torch.float32)[int(rng.integers(2))]
+    m = int(rng.integers(0, 4))
+    eps = float(np.float32(rng.uniform(0.001, 0.05)))
+    noise = rng.uniform(0.0005, 0.05, size=n)
+    say(f"case: seed {seed}, {n} chunks {sizes} from {offs[0]}, {dtype}, m={m} eps={eps:.4g}")
+    x32 = rng.standard_normal(total).astype(np.float32)
+    y32 = x32.copy()
+    for i in range(n):
+        y32[offs[i]:offs[i + 1]] += (noise[i] * rng.standard_normal(sizes[i])).astype(np.float32)
+    x = torch.from_numpy(x32).to(dtype)
+    y = torch.from_numpy(y32).to(dtype)
+    steps = [int(v) for v in rng.integers(-1, 6, size=n)]
+    f0 = [float(np.float32(v)) for v in rng.uniform(0.0, eps, size=n)]
+    dec = fc.ChunkDecider(offs, m, eps, dtype, DEV)
+    dec.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    dec.f.copy_(torch.tensor(f0, dtype=torch.float32))
+    dec.recompute.fill_(9)
+    dec.decide(x.to(DEV), y.to(DEV))
+    torch.cuda.synchronize()
+    l1 = oracle.chunk_l1_rel(x, y, offs)
+    got_l1, got_f = dec.l1.cpu().numpy(), dec.f.cpu().numpy()
+    got_rec, got_step = dec.recompute.cpu().tolist(), dec.step.cpu().tolist()
+    for i in range(n):
+        if steps[i] < 0:  # inactive: untouched
+            assert got_rec[i] == 9 and got_step[i] == steps[i] and got_f[i] == np.float32(f0[i]), i
+            continue
+        assert got_step[i] == steps[i] + 1, i
+        if np.isinf(l1[i]):
+            assert np.isinf(got_l1[i]), i
+        else:
+            assert abs(got_l1[i] - l1[i]) <= parity.L1_RTOL * l1[i] + 1e-12, (i, got_l1[i], l1[i])
+        want_rec, want_f = oracle.decide(steps[i], f0[i], l1[i], m, eps)
+        if steps[i] >= m and abs(f0[i] + l1[i] - eps) <= parity.EPS_BAND:
+            continue  # inside the band either branch is correct
+        assert got_rec[i] == int(want_rec), (i, got_rec[i], want_rec)
+        assert abs(got_f[i] - want_f) <= 1e-6 * max(1.0, abs(want_f)), (i, got_f[i], want_f)
