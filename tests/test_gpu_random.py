@@ -113,3 +113,47 @@ def test_random_chunk_decisions(fc, seed):
             continue  # inside the band either branch is correct
         assert got_rec[i] == int(want_rec), (i, got_rec[i], want_rec)
         assert abs(got_f[i] - want_f) <= 1e-6 * max(1.0, abs(want_f)), (i, got_f[i], want_f)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_euler_steps(fc, seed):
+    # the fused update is bit-exact against the oracle's update on every
+    # active chunk, leaves inactive chunks and the gaps between chunks alone,
+    # and decides exactly as the plain pass on (X_t, the stored X_{t-1})
+    rng = np.random.default_rng(4000 + seed)
+    n = int(rng.integers(1, 9))
+    sizes = [0 if rng.uniform() < 0.1 else int(rng.integers(1, 40000)) for _ in range(n)]
+    offs = [int(rng.integers(0, 9))]
+    for s in sizes:
+        offs.append(offs[-1] + s)
+    total = offs[-1] + int(rng.integers(0, 9))
+    dtype = (torch.bfloat16, torch.float32)[int(rng.integers(2))]
+    m, eps = int(rng.integers(0, 3)), float(np.float32(rng.uniform(0.002, 0.05)))
+    dts = [float(np.float32(v)) for v in -rng.uniform(1e-4, 0.05, size=n)]
+    steps = [int(v) for v in rng.integers(-1, 5, size=n)]
+    say(f"case: seed {seed}, {n} chunks {sizes} from {offs[0]}, {dtype}, steps {steps}")
+    x = torch.from_numpy(rng.standard_normal(total).astype(np.float32)).to(dtype)
+    v = torch.from_numpy((rng.uniform(0.5, 2.0) * rng.standard_normal(total)).astype(np.float32)).to(dtype)
+    y = torch.full((total,), 5.0, dtype=dtype, device=DEV)
+    fused = fc.ChunkDecider(offs, m, eps, dtype, DEV)
+    fused.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    fused.euler_step(x.to(DEV), v.to(DEV), torch.tensor(dts, dtype=torch.float32, device=DEV), y)
+    torch.cuda.synchronize()
+    active = [s >= 0 for s in steps]
+    want = oracle.euler_step(x, v, offs, dts, active)
+    got = y.cpu()
+    for i in range(n):
+        lo, hi = offs[i], offs[i + 1]
+        if active[i]:
+            assert torch.equal(got[lo:hi], want[lo:hi]), i
+        else:
+            assert bool((got[lo:hi] == 5.0).all()), i
+    assert bool((got[:offs[0]] == 5.0).all()) and bool((got[offs[-1]:] == 5.0).all())
+    plain = fc.ChunkDecider(offs, m, eps, dtype, DEV)
+    plain.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    plain.decide(x.to(DEV), y)
+    torch.cuda.synchronize()
+    for name in ("recompute", "f", "step"):
+        assert torch.equal(getattr(fused, name).cpu(), getattr(plain, name).cpu()), name
+    act = torch.tensor(active)
+    assert torch.equal(fused.l1.cpu()[act], plain.l1.cpu()[act])
