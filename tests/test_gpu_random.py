@@ -1,9 +1,10 @@
 """Seeded random sweeps through the C ABI against the fp64 oracle: small
 compressions over every dtype, head size, window, lambda and temperature
 the boundary accepts (with one-query, one-key and budget-above-L_k corners),
-and chunk decisions over random, unaligned chunk tables with random states,
-step counters and accumulators.  The configurations come from fixed seeds,
-so every run draws the same ones."""
+chunk decisions (chunkwise, fused Euler, uniform, history-guided) over
+random, unaligned chunk tables with random states, step counters and
+accumulators, and cache runs with random budgets and commit sizes.  The
+configurations come from fixed seeds, so every run draws the same ones."""
 import numpy as np
 import pytest
 import torch
@@ -157,3 +158,98 @@ def test_random_euler_steps(fc, seed):
         assert torch.equal(getattr(fused, name).cpu(), getattr(plain, name).cpu()), name
     act = torch.tensor(active)
     assert torch.equal(fused.l1.cpu()[act], plain.l1.cpu()[act])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_cache_runs(fc, seed):
+    # random budgets, active sizes, commit sizes (1 .. B_active), query
+    # counts, lambda and windows through KvCache, in lockstep with the
+    # oracle's cache_commit (tests/test_gpu_cache.py)
+    from test_gpu_cache import run_config
+    rng = np.random.default_rng(5000 + seed)
+    dtype = ("bf16", "f32")[int(rng.integers(2))]
+    d = (64, 128)[int(rng.integers(2))]
+    H = int(rng.integers(1, 4))
+    B_budget, B_active = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    sizes = [int(rng.integers(1, B_active + 1)) for _ in range(int(rng.integers(3, 9)))]
+    Lq = int(rng.integers(1, 100))
+    lam = round(float(rng.uniform()), 3)
+    w = int(rng.choice([1, 3, 5, 7]))
+    cfg = synth.CacheConfig("random", H=H, d=d, n_chunks=len(sizes), fpc=1, ny=1, nx=1, B_budget=B_budget,
+                            B_active=B_active, Lq=Lq, lam=lam, w=w, dtype=dtype)
+    say(f"case: seed {seed}, {dtype} d={d} H={H} budget {B_budget} active {B_active} commits {sizes} Lq={Lq} "
+        f"lambda={lam} w={w}")
+    total = sum(sizes)
+    Q, K, V = synth.random_kv(H, Lq, total, d, dtype, seed=6000 + seed)
+    Qs = torch.stack([torch.roll(Q, shifts=c, dims=1) for c in range(3)])
+    cache, _ = run_config(fc, cfg, Qs.to(DEV), K.to(DEV), V.to(DEV), sizes=sizes, label=f"random {seed}")
+    assert cache.length == min(total, B_budget)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_policies(fc, seed):
+    # the uniform rule (one decision for all active chunks) and the
+    # history-guided rule on random tables and states
+    rng = np.random.default_rng(7000 + seed)
+    n = int(rng.integers(1, 10))
+    sizes = [0 if rng.uniform() < 0.1 else int(rng.integers(1, 30000)) for _ in range(n)]
+    offs = [int(rng.integers(0, 9))]
+    for s in sizes:
+        offs.append(offs[-1] + s)
+    total = offs[-1] + 3
+    dtype = (torch.bfloat16, torch.float32)[int(rng.integers(2))]
+    m, eps = int(rng.integers(0, 3)), float(np.float32(rng.uniform(0.005, 0.3)))
+    say(f"case: seed {seed}, {n} chunks {sizes}, {dtype}, m={m} eps={eps:.4g}")
+    x32 = rng.standard_normal(total).astype(np.float32)
+    y32 = x32 + (rng.uniform(0.001, 0.1) * rng.standard_normal(total)).astype(np.float32)
+    x, y = torch.from_numpy(x32).to(dtype), torch.from_numpy(y32).to(dtype)
+    xd, yd = x.to(DEV), y.to(DEV)
+    p = fc.fc_l1_params(n, m, eps, fc.FC_BF16 if dtype == torch.bfloat16 else fc.FC_F32)
+    ws = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p, offs), dtype=torch.uint8, device=DEV)
+    # uniform
+    cstep = [int(v) for v in rng.integers(-1, 3, size=n)]
+    g0, f0 = int(rng.integers(0, 4)), float(np.float32(rng.uniform(0.0, eps)))
+    cs = torch.tensor(cstep, dtype=torch.int32, device=DEV)
+    gs = torch.tensor([g0], dtype=torch.int32, device=DEV)
+    f = torch.tensor([f0], dtype=torch.float32, device=DEV)
+    rec = torch.full((n,), 9, dtype=torch.uint8, device=DEV)
+    l1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fc.fc_uniform_rel_l1_decide(p, offs, xd, yd, cs, gs, f, rec, l1, ws)
+    torch.cuda.synchronize()
+    active = [c >= 0 for c in cstep]
+    got = rec.cpu().tolist()
+    assert all(got[i] == 9 for i in range(n) if not active[i])
+    assert gs.item() == g0 + 1
+    want_l1 = oracle.uniform_l1_rel(x, y, offs, active)
+    if np.isinf(want_l1):
+        assert np.isinf(l1.item())
+    else:
+        assert abs(l1.item() - want_l1) <= parity.L1_RTOL * want_l1 + 1e-12
+    r, fw = oracle.decide(g0, f0, want_l1, m, eps)
+    if not (g0 >= m and abs(f0 + want_l1 - eps) <= parity.EPS_BAND):
+        assert all(got[i] == int(r) for i in range(n) if active[i])
+        assert abs(f.item() - fw) <= 1e-6 * max(1.0, abs(fw))
+    # history-guided
+    hsteps = [int(v) for v in rng.integers(-1, 4, size=n)]
+    acc0 = [float(np.float32(v)) for v in rng.uniform(0.0, eps, size=n)]
+    st = torch.tensor(hsteps, dtype=torch.int32, device=DEV)
+    acc = torch.tensor(acc0, dtype=torch.float32, device=DEV)
+    ref = torch.full((n,), 9, dtype=torch.uint8, device=DEV)
+    dev = torch.zeros(n, dtype=torch.float32, device=DEV)
+    fc.fc_history_rel_l1_decide(p, offs, xd, yd, st, acc, ref, dev, ws)
+    torch.cuda.synchronize()
+    want = oracle.chunk_l1_rel(x, y, offs)
+    g_ref, g_acc, g_st = ref.cpu().tolist(), acc.cpu().numpy(), st.cpu().tolist()
+    for i in range(n):
+        if hsteps[i] < 0:
+            assert g_ref[i] == 9 and g_st[i] == hsteps[i], i
+            continue
+        assert g_st[i] == hsteps[i] + 1, i
+        r, a = oracle.decide_history(hsteps[i], acc0[i], want[i], m, eps)
+        if hsteps[i] >= m and abs(acc0[i] + want[i] - eps) <= parity.EPS_BAND:
+            continue
+        assert g_ref[i] == int(r), (i, g_ref[i], r)
+        if np.isinf(a):
+            assert np.isinf(g_acc[i]), i
+        else:
+            assert abs(g_acc[i] - a) <= 1e-6 * max(1.0, abs(a)), (i, g_acc[i], a)
