@@ -8,6 +8,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def ensure_library() -> str:
+    """Path of libflowcache.so, built first (hipcc cross-compiles for gfx950
+    without a GPU) when it is missing.  For the CPU tests only: a GPU run
+    loads the library built beforehand."""
+    lib = os.path.join(ROOT, "kv_cache_compression_fc_amd", "libflowcache.so")
+    if not os.path.exists(lib):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "flowcache_build", os.path.join(ROOT, "kv_cache_compression_fc_amd", "csrc", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    return lib
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP library)")
     config.addinivalue_line("markers", "slow: long-running CPU test")

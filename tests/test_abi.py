@@ -20,8 +20,8 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def fc():
-    if not os.path.exists(LIB):
-        pytest.fail("libflowcache.so is not built (run __graft_entry__.build())")
+    from conftest import ensure_library
+    ensure_library()
     from kv_cache_compression_fc_amd import binding
     return binding
 

@@ -14,8 +14,8 @@ PKG = os.path.join(ROOT, "kv_cache_compression_fc_amd")
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 def test_c_caller(tmp_path):
-    if not os.path.exists(os.path.join(PKG, "libflowcache.so")):
-        pytest.fail("libflowcache.so is not built (run __graft_entry__.build())")
+    from conftest import ensure_library
+    ensure_library()
     exe = str(tmp_path / "abi_c")
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
                     SRC, "-L", PKG, "-lflowcache", "-Wl,-rpath," + PKG, "-o", exe], check=True)
