@@ -466,6 +466,15 @@ def main() -> int:
         result["cache"] = cache
     if others is not None:
         result["other_shapes"] = others
+    # Context only: the FlowCache page's main table (section on key
+    # experimental data) gives whole-video generation times with the models
+    # on an A800; they include the transformer forwards this library does not
+    # run, so they are not a target for this per-step metric.
+    result["context"] = {
+        "source": "Flow Caching for Autoregressive Video Generation (papernotes digest), main table, A800",
+        "whole_video_latency_s": {"MAGI-1": {"vanilla": 2873, "flowcache_fast": 1209},
+                                  "SkyReels-V2": {"vanilla": 1540, "flowcache_fast": 230}},
+    }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on whole steps")
         result["cpu_baseline"] = cpu_baseline(cfg, ccfg, args.cpu_seconds)
