@@ -25,8 +25,16 @@
  *     and runs asynchronously.  Argument checks happen on the host, before
  *     anything is queued, and return an error code synchronously.
  *   - Outputs must not alias inputs.  Tensors are dense and row-contiguous.
+ *   - Alignment: the base pointers of the row tensors (Q, K, V, K_out,
+ *     V_out, K_chunk, V_chunk, K_clean, V_clean) and of the chunk states
+ *     (X_t, X_tm1, v, X_next, h_prev, h_cur) must be 16-byte aligned (every
+ *     hipMalloc or torch allocation is; a view that starts inside a row may
+ *     not be).  Any other base is FC_ERR_INVALID_ARG.  Float and int32
+ *     arrays (imp, r, lse, scores, idx, step, f, ...) need only their
+ *     natural alignment.
  *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
- *     in [0,1], even pool window, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
+ *     in [0,1], even pool window or one above 129, a row tensor or state not
+ *     16-byte aligned, ...), FC_ERR_UNSUPPORTED (head dim not 64 or
  *     128, unknown dtype, more than 65535 heads, one head's Q or K rows at
  *     2 GiB or more, launch grids beyond a dispatch's 32-bit work-item
  *     count, too many chunks), FC_ERR_WORKSPACE (workspace null,
@@ -73,8 +81,8 @@ typedef enum { FC_F32 = 0, FC_BF16 = 1 } fc_dtype;
  *   L_k          clean keys in the cache before compression
  *   B_budget     tokens each head keeps; B' = min(B_budget, L_k)
  *   lambda       importance weight in [0,1]
- *   pool_window  odd max-pool window w >= 1 (stride 1, same size, positions
- *                outside [0, L_k) ignored, along the token order)
+ *   pool_window  odd max-pool window, 1 <= w <= 129 (stride 1, same size,
+ *                positions outside [0, L_k) ignored, along the token order)
  *   softmax_scale attention temperature; 0 means 1/sqrt(d)
  *   dtype        FC_BF16 or FC_F32 for Q, K, V and K_out, V_out
  */
@@ -110,7 +118,11 @@ size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
  * normalised with max(||k||, 1e-12) and so contribute no similarity.  A
  * key's squared norm is summed in float32: keys whose squared norm exceeds
  * the float32 range (elements beyond about 1e19) are outside the domain.
- * Deterministic: identical inputs give bit-identical outputs.
+ * Deterministic on one device model: identical inputs give bit-identical
+ * outputs.  The importance passes split their work from the device's compute
+ * unit count and occupancy, which fixes the float32 summation order; a
+ * device of another model may round differently (within the float32
+ * accuracy of the sums).
  */
 fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, const void* V,
                          void* K_out, void* V_out, int32_t* idx_out,

@@ -184,6 +184,20 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
     return workspace
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    """Size in bytes of a workspace tensor of any dtype (0 for None, which the
+    library answers with FC_ERR_WORKSPACE)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _chunk_workspace(p: fc_l1_params, chunk_offsets: Sequence[int], workspace: Optional[torch.Tensor],
+                     device) -> torch.Tensor:
+    """The caller's workspace, or one sized by the query when none is given."""
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(fc_chunk_rel_l1_workspace_bytes(p, chunk_offsets), 1), dtype=torch.uint8, device=device)
+
+
 def fc_kv_compress(Q, K, V, B_budget: int, lam: float, pool_window: int, softmax_scale: float = 0.0,
                    want_scores: bool = False, out: Optional[Dict[str, torch.Tensor]] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
@@ -211,7 +225,7 @@ def fc_kv_compress(Q, K, V, B_budget: int, lam: float, pool_window: int, softmax
     _check("fc_kv_compress", _lib.fc_kv_compress(
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(out["K_out"]), _ptr(out["V_out"]), _ptr(out["idx"]),
         _ptr(out.get("score")), _ptr(out.get("imp_pooled")), _ptr(out.get("red")),
-        _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(ws), _nbytes(ws), _stream(stream)))
     return out
 
 
@@ -223,7 +237,7 @@ def fc_kv_importance(Q, K, softmax_scale: float = 0.0, imp_out=None, workspace=N
     _expect("imp_out", imp_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance", _lib.fc_kv_importance(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(imp_out), _ptr(ws),
-                                                     ws.numel(), _stream(stream)))
+                                                     _nbytes(ws), _stream(stream)))
     return imp_out
 
 
@@ -235,7 +249,7 @@ def fc_kv_importance_lse(Q, K, softmax_scale: float = 0.0, lse_out=None, workspa
     _expect("lse_out", lse_out, (H, Lq), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance_lse", _lib.fc_kv_importance_lse(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse_out),
-                                                             _ptr(ws), ws.numel(), _stream(stream)))
+                                                             _ptr(ws), _nbytes(ws), _stream(stream)))
     return lse_out
 
 
@@ -248,7 +262,7 @@ def fc_kv_importance_colsum(Q, K, lse, softmax_scale: float = 0.0, imp_out=None,
     _expect("imp_out", imp_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
     _check("fc_kv_importance_colsum", _lib.fc_kv_importance_colsum(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(lse),
-                                                                   _ptr(imp_out), _ptr(ws), ws.numel(),
+                                                                   _ptr(imp_out), _ptr(ws), _nbytes(ws),
                                                                    _stream(stream)))
     return imp_out
 
@@ -260,7 +274,7 @@ def fc_kv_redundancy(K, r_out=None, workspace=None, stream=None) -> torch.Tensor
         r_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
     _expect("r_out", r_out, (H, Lk), torch.float32)
     ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
-    _check("fc_kv_redundancy", _lib.fc_kv_redundancy(ctypes.byref(p), _ptr(K), _ptr(r_out), _ptr(ws), ws.numel(),
+    _check("fc_kv_redundancy", _lib.fc_kv_redundancy(ctypes.byref(p), _ptr(K), _ptr(r_out), _ptr(ws), _nbytes(ws),
                                                      _stream(stream)))
     return r_out
 
@@ -290,7 +304,7 @@ def fc_kv_select(imp, r, B_budget: int, lam: float, pool_window: int, K=None, V=
     _check("fc_kv_select", _lib.fc_kv_select(
         ctypes.byref(p), _ptr(imp), _ptr(r), _ptr(K), _ptr(V), _ptr(out.get("K_out")), _ptr(out.get("V_out")),
         _ptr(out["idx"]), _ptr(out.get("score")), _ptr(out.get("imp_pooled")), _ptr(out.get("red")),
-        _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(ws), _nbytes(ws), _stream(stream)))
     return out
 
 
@@ -305,7 +319,7 @@ def fc_topb_select(scores: torch.Tensor, B: int, idx_out=None, workspace=None, s
         idx_out = torch.empty((H, min(int(B), L)), dtype=torch.int32, device=scores.device)
     _expect("idx_out", idx_out, (H, min(int(B), L)), torch.int32)
     ws = _workspace(fc_topb_select_workspace_bytes(H, L), scores.device, workspace)
-    _check("fc_topb_select", _lib.fc_topb_select(H, L, int(B), _ptr(scores), _ptr(idx_out), _ptr(ws), ws.numel(),
+    _check("fc_topb_select", _lib.fc_topb_select(H, L, int(B), _ptr(scores), _ptr(idx_out), _ptr(ws), _nbytes(ws),
                                                  _stream(stream)))
     return idx_out
 
@@ -365,9 +379,10 @@ def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X
     _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("X_tm1", X_tm1)),
                         (("step", step, n, torch.int32), ("f", f, n, torch.float32),
                          ("recompute", recompute, n, torch.uint8), ("l1_rel_out", l1_rel_out, n, torch.float32)))
+    workspace = _chunk_workspace(p, chunk_offsets, workspace, X_t.device)
     _check("fc_chunk_rel_l1_decide", _lib.fc_chunk_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
-        _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(l1_rel_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def fc_cache_commit_workspace_bytes(c: fc_cache_params, L_q: int) -> int:
@@ -391,7 +406,7 @@ def fc_cache_commit(c: fc_cache_params, L_clean: int, K_chunk, V_chunk, pos0: in
     _check("fc_cache_commit", _lib.fc_cache_commit(
         ctypes.byref(c), ctypes.byref(n), _ptr(K_chunk), _ptr(V_chunk), int(K_chunk.shape[1]), int(pos0), _ptr(Q),
         L_q, _ptr(K_clean), _ptr(V_clean), _ptr(pos_clean), _ptr(workspace),
-        workspace.numel() if workspace is not None else 0, _stream(stream)))
+        _nbytes(workspace), _stream(stream)))
     return int(n.value)
 
 
@@ -428,9 +443,10 @@ def fc_euler_step_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, 
     _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("v", v), ("X_next", X_next)),
                         (("dt", dt, n, torch.float32), ("step", step, n, torch.int32), ("f", f, n, torch.float32),
                          ("recompute", recompute, n, torch.uint8), ("l1_rel_out", l1_rel_out, n, torch.float32)))
+    workspace = _chunk_workspace(p, chunk_offsets, workspace, X_t.device)
     _check("fc_euler_step_l1_decide", _lib.fc_euler_step_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(v), _ptr(dt), _ptr(X_next), _ptr(step), _ptr(f),
-        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def fc_uniform_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, chunk_step, step, f,
@@ -440,9 +456,10 @@ def fc_uniform_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t,
                         (("chunk_step", chunk_step, n, torch.int32), ("step", step, 1, torch.int32),
                          ("f", f, 1, torch.float32), ("recompute", recompute, n, torch.uint8),
                          ("l1_rel_out", l1_rel_out, 1, torch.float32)))
+    workspace = _chunk_workspace(p, chunk_offsets, workspace, X_t.device)
     _check("fc_uniform_rel_l1_decide", _lib.fc_uniform_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(chunk_step), _ptr(step), _ptr(f),
-        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(recompute), _ptr(l1_rel_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def fc_history_rel_l1_decide(p: fc_l1_params, segment_offsets: Sequence[int], h_prev, h_cur, step, acc, refresh,
@@ -451,6 +468,7 @@ def fc_history_rel_l1_decide(p: fc_l1_params, segment_offsets: Sequence[int], h_
     _expect_chunk_state(p, segment_offsets, (("h_prev", h_prev), ("h_cur", h_cur)),
                         (("step", step, n, torch.int32), ("acc", acc, n, torch.float32),
                          ("refresh", refresh, n, torch.uint8), ("dev_out", dev_out, n, torch.float32)))
+    workspace = _chunk_workspace(p, segment_offsets, workspace, h_prev.device)
     _check("fc_history_rel_l1_decide", _lib.fc_history_rel_l1_decide(
         ctypes.byref(p), _offsets(segment_offsets), _ptr(h_prev), _ptr(h_cur), _ptr(step), _ptr(acc), _ptr(refresh),
-        _ptr(dev_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(dev_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))

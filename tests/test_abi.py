@@ -238,3 +238,58 @@ def test_binding_refuses_mismatched_tensors(fc):
     with pytest.raises(ValueError, match="on the GPU"):  # consistent arguments reach the device check
         fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 8, 64, dtype=bf), 0, None, Kc, Kc,
                            pos, ws)
+
+
+def test_pool_window_cap_and_alignment_rule(fc):
+    """The contract's limits: 1 <= pool_window <= 129 and odd; row tensors and
+    chunk states 16-byte aligned (FC_ERR_INVALID_ARG otherwise)."""
+    assert fc.fc_kv_compress_workspace_bytes(_params(fc, pool_window=129)) > 0
+    assert fc.fc_kv_compress_workspace_bytes(_params(fc, pool_window=131)) == 0
+    lib = fc._lib
+    p = _params(fc)
+    need = fc.fc_kv_compress_workspace_bytes(p)
+    ws = ctypes.c_void_p(1 << 20)
+    a = ctypes.c_void_p(4096)
+    for bad in range(5):  # Q, K, V, K_out, V_out each 8 bytes off a 16-byte boundary
+        ptrs = [a] * 5
+        ptrs[bad] = ctypes.c_void_p(4096 + 8)
+        st = lib.fc_kv_compress(ctypes.byref(p), *ptrs, a, None, None, None, ws, need, None)
+        assert st == fc.FC_ERR_INVALID_ARG, bad
+    st = lib.fc_kv_compress(ctypes.byref(_params(fc, pool_window=131)), a, a, a, a, a, a, None, None, None, ws,
+                            need, None)
+    assert st == fc.FC_ERR_INVALID_ARG
+    # chunk states: the fused Euler step checks X_t, v and X_next
+    pl = fc.fc_l1_params(2, 1, 0.01, fc.FC_BF16)
+    offs = fc._offsets([0, 64, 128])
+    n = fc.fc_chunk_rel_l1_workspace_bytes(pl, [0, 64, 128])
+    for bad in range(3):
+        ptrs = [a] * 3
+        ptrs[bad] = ctypes.c_void_p(4096 + 8)
+        st = lib.fc_euler_step_l1_decide(ctypes.byref(pl), offs, ptrs[0], ptrs[1], a, ptrs[2], a, a, a, None, ws, n,
+                                         None)
+        assert st == fc.FC_ERR_INVALID_ARG, bad
+    # no workspace at all is a workspace error, not a crash
+    st = lib.fc_chunk_rel_l1_decide(ctypes.byref(pl), offs, a, a, a, a, a, None, None, 0, None)
+    assert st == fc.FC_ERR_WORKSPACE
+
+
+def test_binding_workspace_sizes(fc):
+    """Workspace sizes cross the boundary in bytes whatever the tensor's
+    dtype, and the chunk-decision wrappers size their own workspace when none
+    is given (here the CPU tensors then stop at the device check, not at an
+    AttributeError)."""
+    import torch
+    assert fc._nbytes(None) == 0
+    assert fc._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
+    assert fc._nbytes(torch.zeros(10, dtype=torch.uint8)) == 10
+    bf = torch.bfloat16
+    offs = [0, 100, 250]
+    p = fc.fc_l1_params(2, 1, 0.01, fc.FC_BF16)
+    st, f, rec = torch.zeros(2, dtype=torch.int32), torch.zeros(2), torch.zeros(2, dtype=torch.uint8)
+    x = torch.zeros(250, dtype=bf)
+    for call in (lambda: fc.fc_chunk_rel_l1_decide(p, offs, x, x, st, f, rec),
+                 lambda: fc.fc_euler_step_l1_decide(p, offs, x, x, torch.zeros(2), x, st, f, rec),
+                 lambda: fc.fc_uniform_rel_l1_decide(p, offs, x, x, st, st[:1], f[:1], rec),
+                 lambda: fc.fc_history_rel_l1_decide(p, offs, x, x, st, f, rec)):
+        with pytest.raises(ValueError, match="on the GPU"):
+            call()
