@@ -301,6 +301,27 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fc_chunk_rel_l1_decide_noalloc -- fc_chunk_rel_l1_decide for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument and no allocation
+ * of any kind.  The slab partials live in a static device array of
+ * FC_NOALLOC_SCRATCH_BYTES per device (one float2 per slab of 32768 bf16 or
+ * 16384 float32 elements, each chunk rounded up to whole slabs: about 1.07e9
+ * bf16 or 5.4e8 float32 elements in all), held until the process ends.
+ * Arguments, results and errors as for fc_chunk_rel_l1_decide, the same
+ * kernels and the same bits; states beyond the array's slabs are
+ * FC_ERR_UNSUPPORTED (checked on the host, before anything touches the
+ * device).  Every call on one device shares that device's array, so calls
+ * that overlap in time on one device (different streams, or threads without
+ * ordering) race and must not be made; calls ordered on one stream are safe.
+ */
+#define FC_NOALLOC_SCRATCH_BYTES ((size_t)256 * 1024)
+fc_status fc_chunk_rel_l1_decide_noalloc(const fc_l1_params* p, const int64_t* chunk_offsets,
+                                         const void* X_t, const void* X_tm1,
+                                         int32_t* step, float* f, uint8_t* recompute, float* l1_rel_out,
+                                         void* stream);
+
+/*
  * fc_euler_step_l1_decide -- the sampler's Euler step with the decision fused.
  * Item 1 writes the L1 numerator as ||v dt||_1: the update X_{t-1} = X_t + v dt
  * itself.  For every active chunk i:

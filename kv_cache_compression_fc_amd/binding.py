@@ -35,8 +35,9 @@ EXPORTS = (
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
     "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
     "fc_cache_commit_workspace_bytes", "fc_cache_commit", "fc_euler_step_l1_decide",
-    "fc_uniform_rel_l1_decide", "fc_history_rel_l1_decide",
+    "fc_uniform_rel_l1_decide", "fc_history_rel_l1_decide", "fc_chunk_rel_l1_decide_noalloc",
 )
+FC_NOALLOC_SCRATCH_BYTES = 256 * 1024
 
 
 class fc_kv_params(ctypes.Structure):
@@ -84,6 +85,9 @@ _lib.fc_chunk_rel_l1_workspace_bytes.argtypes = [ctypes.POINTER(fc_l1_params), _
 _lib.fc_chunk_rel_l1_decide.restype = ctypes.c_int
 _lib.fc_chunk_rel_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]
+_lib.fc_chunk_rel_l1_decide_noalloc.restype = ctypes.c_int
+_lib.fc_chunk_rel_l1_decide_noalloc.argtypes = [ctypes.POINTER(fc_l1_params), _i64p, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp]
 
 _lib.fc_cache_commit_workspace_bytes.restype = _sz
 _lib.fc_cache_commit_workspace_bytes.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.c_int32]
@@ -383,6 +387,19 @@ def fc_chunk_rel_l1_decide(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X
     _check("fc_chunk_rel_l1_decide", _lib.fc_chunk_rel_l1_decide(
         ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
         _ptr(l1_rel_out), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def fc_chunk_rel_l1_decide_noalloc(p: fc_l1_params, chunk_offsets: Sequence[int], X_t, X_tm1, step, f, recompute,
+                                   l1_rel_out=None, stream=None) -> None:
+    """fc_chunk_rel_l1_decide without a workspace: the library's static
+    per-device scratch holds the slab partials (nothing is allocated)."""
+    n = p.n_chunks
+    _expect_chunk_state(p, chunk_offsets, (("X_t", X_t), ("X_tm1", X_tm1)),
+                        (("step", step, n, torch.int32), ("f", f, n, torch.float32),
+                         ("recompute", recompute, n, torch.uint8), ("l1_rel_out", l1_rel_out, n, torch.float32)))
+    _check("fc_chunk_rel_l1_decide_noalloc", _lib.fc_chunk_rel_l1_decide_noalloc(
+        ctypes.byref(p), _offsets(chunk_offsets), _ptr(X_t), _ptr(X_tm1), _ptr(step), _ptr(f), _ptr(recompute),
+        _ptr(l1_rel_out), _stream(stream)))
 
 
 def fc_cache_commit_workspace_bytes(c: fc_cache_params, L_q: int) -> int:

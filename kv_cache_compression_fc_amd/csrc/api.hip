@@ -3,6 +3,8 @@
 // include/flowcache.h.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/flowcache.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -203,6 +205,31 @@ fc_status chunk_table(const fc_l1_params* p, const int64_t* off, ChunkTable* tab
 }
 
 size_t chunk_ws_bytes(const ChunkTable& tab) { return align_up((size_t)tab.blk_start[tab.n] * sizeof(float2)); }
+
+// ---- allocation-free chunk decision ---------------------------------------------------------
+// The slab partials of fc_chunk_rel_l1_decide_noalloc live in this array, one
+// copy per device, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current.
+constexpr size_t kNoAllocScratchBytes = FC_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// The device address of this device's scratch array (nullptr on failure).
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        // two threads racing here look up the same address; either store wins
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
 
 }  // namespace
 
@@ -424,6 +451,23 @@ fc_status fc_chunk_rel_l1_decide(const fc_l1_params* p, const int64_t* chunk_off
     return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, step, f, recompute, l1_rel_out,
                                       static_cast<float2*>(workspace), p->m, p->eps,
                                       static_cast<hipStream_t>(stream)));
+}
+
+fc_status fc_chunk_rel_l1_decide_noalloc(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,
+                                         const void* X_tm1, int32_t* step, float* f, uint8_t* recompute,
+                                         float* l1_rel_out, void* stream) {
+    ChunkTable tab;
+    fc_status st = chunk_table(p, chunk_offsets, &tab);
+    if (st != FC_OK) return st;
+    if (!X_t || !X_tm1 || !step || !f || !recompute) return FC_ERR_INVALID_ARG;
+    if (!aligned16(X_t) || !aligned16(X_tm1)) return FC_ERR_INVALID_ARG;
+    if (chunk_ws_bytes(tab) > kNoAllocScratchBytes) return FC_ERR_UNSUPPORTED;  // states beyond the scratch's slabs
+    void* ptr = scratch_ptr();
+    if (ptr == nullptr) return FC_ERR_HIP;
+    const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
+    // every slab partial is written before it is read: nothing to clear
+    return hip_status(launch_chunk_l1(dt, tab, X_t, X_tm1, step, f, recompute, l1_rel_out, static_cast<float2*>(ptr),
+                                      p->m, p->eps, static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_euler_step_l1_decide(const fc_l1_params* p, const int64_t* chunk_offsets, const void* X_t,

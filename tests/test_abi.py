@@ -293,3 +293,25 @@ def test_binding_workspace_sizes(fc):
                  lambda: fc.fc_history_rel_l1_decide(p, offs, x, x, st, f, rec)):
         with pytest.raises(ValueError, match="on the GPU"):
             call()
+
+
+def test_noalloc_decision_limits(fc):
+    """The allocation-free decision refuses, on the host, states whose slabs
+    exceed its static scratch, and checks its arguments as the workspace form
+    does (no device is touched on these paths)."""
+    lib = fc._lib
+    a = ctypes.c_void_p(4096)
+    assert fc.FC_NOALLOC_SCRATCH_BYTES == 256 * 1024
+    # bf16 slabs hold 32768 elements: 8192 slabs (64 KiB of partials) fit,
+    # 2 x 2^30 elements (65536 slabs, 512 KiB) do not
+    p = fc.fc_l1_params(2, 1, 0.01, fc.FC_BF16)
+    big = fc._offsets([0, 1 << 30, 1 << 31])
+    assert lib.fc_chunk_rel_l1_decide_noalloc(ctypes.byref(p), big, a, a, a, a, a, None, None) == fc.FC_ERR_UNSUPPORTED
+    assert fc.fc_chunk_rel_l1_workspace_bytes(p, [0, 1 << 30, 1 << 31]) > fc.FC_NOALLOC_SCRATCH_BYTES
+    small = fc._offsets([0, 64, 128])
+    assert lib.fc_chunk_rel_l1_decide_noalloc(ctypes.byref(p), small, None, a, a, a, a, None, None) == \
+        fc.FC_ERR_INVALID_ARG
+    assert lib.fc_chunk_rel_l1_decide_noalloc(ctypes.byref(p), small, ctypes.c_void_p(4104), a, a, a, a, None,
+                                              None) == fc.FC_ERR_INVALID_ARG
+    assert lib.fc_chunk_rel_l1_decide_noalloc(ctypes.byref(fc.fc_l1_params(0, 1, 0.01, fc.FC_BF16)), small, a, a, a,
+                                              a, a, None, None) == fc.FC_ERR_INVALID_ARG
