@@ -56,7 +56,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.nbu = red_nbu(p->L_k);
     L.nbr = red_nbr(p->L_k);
     L.nkb = imp_colsum_blocks(p->L_k);
-    L.fits = imp_grids_fit(p->H, p->L_q, p->L_k, L.plan, L.nbu);
+    L.fits = imp_grids_fit(p->H, p->L_q, p->L_k, L.plan, L.nbu) && sel_grid_fits(p->H, p->L_k);
     const size_t H = (size_t)p->H, Lk = (size_t)p->L_k;
     size_t o = 0;
     L.part = o;     o = align_up(o + H * L.plan.nsplit * (size_t)p->L_q * sizeof(float2));
@@ -66,7 +66,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.u_part = o;   o = align_up(o + H * L.nbu * (size_t)p->d * sizeof(float));
     L.u = o;        o = align_up(o + H * (size_t)p->d * sizeof(float));
     L.red_part = o; o = align_up(o + H * (size_t)(L.nbr > L.nkb ? L.nbr : L.nkb) * sizeof(float2));
-    L.keys = o;     o = align_up(o + H * Lk * sizeof(uint32_t));
+    L.keys = o;     o = align_up(o + sel_ws_bytes(p->H, p->L_k));  // selection: keys, histograms, counts
     L.total = o;
     return L;
 }
@@ -353,14 +353,14 @@ fc_status fc_kv_select(const fc_kv_params* p, const float* imp, const float* r, 
 }
 
 size_t fc_topb_select_workspace_bytes(int32_t H, int32_t L) {
-    if (H < 1 || L < 1 || H > 65535) return 0;
-    return align_up((size_t)H * (size_t)L * sizeof(uint32_t));  // keys
+    if (H < 1 || L < 1 || H > 65535 || !sel_grid_fits(H, L)) return 0;
+    return align_up(sel_ws_bytes(H, L));  // keys, histograms, counts
 }
 
 fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, int32_t* idx_out, void* workspace,
                          size_t workspace_bytes, void* stream) {
     if (H < 1 || L < 1 || B < 1 || !scores || !idx_out) return FC_ERR_INVALID_ARG;
-    if (H > 65535) return FC_ERR_UNSUPPORTED;
+    if (H > 65535 || !sel_grid_fits(H, L)) return FC_ERR_UNSUPPORTED;
     const size_t need = fc_topb_select_workspace_bytes(H, L);
     if (!ws_ok(workspace, workspace_bytes, need)) return FC_ERR_WORKSPACE;
     const int Bp = B < L ? B : L;

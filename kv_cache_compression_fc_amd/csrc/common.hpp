@@ -111,6 +111,14 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// The hardware hands linear block b to XCD b % 8.  Give every XCD a
+// contiguous range of logical work items (grid padded to a multiple of 8,
+// per_xcd = grid / 8), so that the blocks running together on one XCD share
+// a head and a key (or query) range in that XCD's L2.
+__device__ __forceinline__ int xcd_item(int per_xcd) {
+    return (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
+}
+
 // Merge of two partial softmax normalisers (m, s) meaning s * 2^m.
 __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
     float mn = fmaxf(m, m2);

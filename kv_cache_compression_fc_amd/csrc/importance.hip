@@ -147,13 +147,6 @@ __device__ __forceinline__ void tile_barrier() {
 
 template <int B> using Buf = std::integral_constant<int, B>;
 
-// The hardware hands linear block b to XCD b % 8.  Give every XCD a
-// contiguous range of logical work items, so that the blocks running together
-// on one XCD share a head and a key (or query) range in that XCD's L2.
-__device__ __forceinline__ int xcd_item(int per_xcd) {
-    return (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
-}
-
 #define FC_SB() __builtin_amdgcn_sched_barrier(0)
 
 // acc = (32 streamed rows starting at row r0 of the tile) x (register operand):

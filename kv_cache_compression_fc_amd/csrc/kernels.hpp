@@ -69,12 +69,16 @@ hipError_t launch_red_dot(int dt, int d, const void* K, const float* u_part, flo
 hipError_t launch_red_stats(const float* r, float2* red_part, int H, int Lk, hipStream_t s);
 
 // ---- selection ----------------------------------------------------------------
-// One workgroup per head: scores (from importance + redundancy when r != nullptr,
-// else `src` holds them), order-preserving keys (spilled to keys [H][L] when a
-// head exceeds one chunk), radix select of the B' largest and the ordered
-// compaction into idx_out [H][Bp].
+// Scores (from importance + redundancy when r != nullptr, else `src` holds
+// them), order-preserving keys, radix select of the B' largest and the ordered
+// compaction into idx_out [H][Bp].  Heads of one chunk take one workgroup per
+// head; longer heads split over several workgroups per head (four launches).
+// `keys` is the selection workspace of sel_ws_bytes(H, L) bytes.
 // With r != nullptr, `src` holds nsrc planes [nsrc][H][L] of importance that
 // add up to it.
+size_t sel_ws_bytes(int H, int L);
+// Whether the split selection's launch grids fit a dispatch's 32-bit work-item count.
+bool sel_grid_fits(int H, int L);
 hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
                            int L, int Bp, int32_t* idx_out, hipStream_t s);

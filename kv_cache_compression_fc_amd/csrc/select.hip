@@ -47,8 +47,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum.
+// Exclusive prefix sum over a workgroup of NT threads; *total receives the
+// sum.  `lds` holds NT/64 words.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+    constexpr int kWaves = NT / kWave;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t inc = v;
 #pragma unroll
@@ -60,7 +63,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
         const uint32_t x = lds[w];
         before += w < wave ? x : 0u;
         tot += x;
@@ -73,10 +76,10 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
 // The bin of an LDS histogram of BINS bins, each kept in COPIES copies
 // (word bin*COPIES + copy), that holds the k-th largest element (k >= 1), and
 // k minus the count of the higher bins; every thread gets both.
-template <int BINS, int COPIES>
+template <int BINS, int COPIES, int NT = kSelThreads>
 __device__ __forceinline__ uint32_t find_bin_from_top(const uint32_t* hist, uint32_t k, uint32_t* k_in_bin,
                                                       uint32_t* scan_lds, uint32_t* s_res) {
-    constexpr int kPerT = BINS >= kSelThreads ? BINS / kSelThreads : 1;
+    constexpr int kPerT = BINS >= NT ? BINS / NT : 1;
     constexpr int kActive = BINS / kPerT;
     // thread t owns bins BINS-1-(t*kPerT + i): descending order
     uint32_t cnt[kPerT];
@@ -93,7 +96,7 @@ __device__ __forceinline__ uint32_t find_bin_from_top(const uint32_t* hist, uint
         sum += c;
     }
     uint32_t total;
-    const uint32_t before = block_exclusive_scan(sum, scan_lds, &total);
+    const uint32_t before = block_exclusive_scan<NT>(sum, scan_lds, &total);
     if (sum > 0 && before < k && k <= before + sum) {
         uint32_t acc = before;
         for (int i = 0; i < kPerT; ++i) {
@@ -419,6 +422,357 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
     }
 }
 
+// ---- selection split over several workgroups per head ----------------------------------
+// For heads longer than one workgroup's share, the same exact selection runs
+// as four launches of G workgroups per head, each workgroup owning S
+// consecutive keys [g S, g S + S):
+//   keys:    pool + score + order-preserving key of its keys, written to the
+//            workspace, and the workgroup's histogram of the top 8 key bits;
+//            it also clears the head's round-1 and round-2 histograms;
+//   round 1: the head's round-0 histogram (sum of the G partial ones) gives
+//            the bin b0 of the B'-th largest key; the workgroup counts bits
+//            23..12 of its keys in bin b0 and adds its nonzero bins into the
+//            head's histogram with integer atomics (the counts, and so every
+//            later step, do not depend on their order);
+//   round 2: likewise for bits 11..0 of the keys whose top 20 bits are the
+//            prefix found so far; the workgroup also writes how many of its
+//            keys lie above that prefix and its counts per low-12-bit bin as
+//            suffix sums, so the compaction can count the keys of earlier
+//            workgroups above and at the threshold with two reads each;
+//   compact: the threshold key T and the number q of keys equal to T that
+//            fit come from the head's round-2 histogram; the workgroup's
+//            output offset is the kept keys of the earlier workgroups, and its
+//            kept indices (every key > T, the equal keys while fewer than q
+//            lie before them in token order) go out ascending.
+// Separate launches order the phases: no grid barrier, no spin-wait.
+constexpr int kMT = 512;                  // threads per workgroup
+constexpr int kMWaves = kMT / kWave;
+constexpr int kMKpt = 16;                 // consecutive keys per thread
+constexpr int kMMaxKeys = kMT * kMKpt;    // 8192: most keys one workgroup owns
+constexpr int kRBins = 4096;              // bins of rounds 1 and 2
+constexpr int kRCopies = 4;               // LDS copies of each round-1/2 bin
+constexpr int kR0Copies = 8;              // LDS copies of each round-0 bin
+constexpr int kCum = kRBins + 4;          // per-workgroup suffix counts (4097 used)
+static_assert(kMMaxKeys < 65536, "packed 16-bit counts of one workgroup");
+
+// Workspace of the split selection, per head h and workgroup g.
+struct MselWs {
+    uint32_t* keys;   // [H][L] order-preserving keys
+    uint32_t* hist0;  // [H][G][256] round-0 counts per workgroup
+    uint32_t* h1;     // [H][4096] round-1 counts of the head
+    uint32_t* h2;     // [H][4096] round-2 counts of the head
+    uint32_t* gt20;   // [H][G] keys above the 20-bit prefix per workgroup
+    uint32_t* cum2;   // [H][G][kCum] suffix counts of the prefix-matching keys per low-12-bit bin
+    uint32_t* state;  // [H][4] b0, k1, b1, k2
+};
+
+template <bool kFromImp>
+__global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict__ src, int nsrc,
+                                                        const float* __restrict__ r,
+                                                        const float2* __restrict__ red_part, int nbr, float lam,
+                                                        int hw, float* __restrict__ score_out,
+                                                        float* __restrict__ imp_pooled_out,
+                                                        float* __restrict__ red_out, int H, int L, int G, int S,
+                                                        MselWs ws) {
+    // it[kMaxHalo + x] = importance of key j0 + x (x in [-kMaxHalo, S + kMaxHalo),
+    // -inf outside [0, L)); kt[x]: r (or the score) of key j0 + x, then its key
+    __shared__ __align__(16) float it[kMMaxKeys + 2 * kMaxHalo];
+    __shared__ __align__(16) uint32_t kt[kMMaxKeys];
+    __shared__ uint32_t hist[256 * kR0Copies];
+    __shared__ float stat[2];
+    const int n_items = H * G;
+    const int item = xcd_item((int)(gridDim.x / 8u));
+    if (item >= n_items) return;
+    const int h = item / G, g = item % G, tid = threadIdx.x;
+    const int j0 = g * S, n = min(S, L - j0);
+    const size_t hL = (size_t)h * L;
+    const size_t plane = (size_t)H * L;
+
+    for (int b = tid; b < 256 * kR0Copies; b += kMT) hist[b] = 0u;
+    const float* rs = (kFromImp ? r : src) + hL + j0;
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n) kt[i] = __float_as_uint(rs[i]);
+    }
+    if constexpr (kFromImp) {
+        constexpr int kQa = (kMMaxKeys + 2 * kMaxHalo + kMT - 1) / kMT;
+#pragma unroll
+        for (int q = 0; q < kQa; ++q) {
+            const int i = tid + q * kMT;
+            if (i < n + 2 * kMaxHalo) {
+                const int j = j0 - kMaxHalo + i;
+                float v = -INFINITY;
+                if (j >= 0 && j < L) {
+                    v = src[hL + j];
+                    for (int pl = 1; pl < nsrc; ++pl) v += src[pl * plane + hL + j];
+                }
+                it[i] = v;
+            }
+        }
+        // softmax statistics of r: (max of r log2 e, 1 / sum 2^{r log2 e - max})
+        if (tid < kWave) {
+            float M = -1e30f, Sm = 0.f;
+            for (int i = tid; i < nbr; i += kWave) {
+                const float2 v = red_part[(size_t)h * nbr + i];
+                lse2_merge(M, Sm, v.x, v.y);
+            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(Sm, o, kWave);
+                lse2_merge(M, Sm, m2, s2);
+            }
+            if (tid == 0) {
+                stat[0] = M;
+                stat[1] = 1.0f / Sm;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int x0 = tid * kMKpt;
+    const uint32_t copy = tid & (kR0Copies - 1);
+    float pooled[kMKpt];
+    if constexpr (kFromImp) {
+        if (hw <= kRegHalo) {
+            float v[kMKpt + 2 * kRegHalo];
+#pragma unroll
+            for (int q = 0; q < kMKpt + 2 * kRegHalo; ++q) v[q] = it[kMaxHalo - kRegHalo + x0 + q];
+#pragma unroll
+            for (int i = 0; i < kMKpt; ++i) {
+                float p = v[kRegHalo + i];
+#pragma unroll
+                for (int o = 1; o <= kRegHalo; ++o)
+                    if (o <= hw) p = fmaxf(p, fmaxf(v[kRegHalo + i - o], v[kRegHalo + i + o]));
+                pooled[i] = p;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMKpt; ++i) {
+                const float* t = it + kMaxHalo + x0 + i;
+                float p = t[0];
+                for (int o = 1; o <= hw; ++o) p = fmaxf(p, fmaxf(t[-o], t[o]));
+                pooled[i] = p;
+            }
+        }
+    }
+    const float M = kFromImp ? stat[0] : 0.f, invS = kFromImp ? stat[1] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kMKpt; ++i) {
+        const int x = x0 + i;
+        if (x < n) {
+            const float v = __uint_as_float(kt[x]);
+            float sc = v;
+            if constexpr (kFromImp) {
+                const float red = exp2_hw(fmaf(v, kLog2e, -M)) * invS;
+                sc = lam * pooled[i] - (1.0f - lam) * red;
+                const size_t j = hL + j0 + x;
+                if (score_out) score_out[j] = sc;
+                if (imp_pooled_out) imp_pooled_out[j] = pooled[i];
+                if (red_out) red_out[j] = red;
+            }
+            const uint32_t key = order_key(sc);
+            kt[x] = key;  // this thread's own slot
+            atomicAdd(&hist[(key >> 24) * kR0Copies + copy], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* kg = ws.keys + hL + j0;
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n) kg[i] = kt[i];
+    }
+    if (tid < 256) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int cp = 0; cp < kR0Copies; ++cp) c += hist[tid * kR0Copies + cp];
+        ws.hist0[((size_t)h * G + g) * 256 + tid] = c;
+    }
+    // the head's round-1 and round-2 histograms start at zero
+    for (int b = g * kMT + tid; b < kRBins; b += G * kMT) {
+        ws.h1[(size_t)h * kRBins + b] = 0u;
+        ws.h2[(size_t)h * kRBins + b] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kMT) void msel_round1_kernel(int H, int L, int G, int S, int Bp, MselWs ws) {
+    __shared__ uint32_t hist[kRBins * kRCopies];
+    __shared__ uint32_t tot0[256];
+    __shared__ uint32_t scan_lds[kMWaves];
+    __shared__ uint32_t s_res[2];
+    const int item = xcd_item((int)(gridDim.x / 8u));
+    if (item >= H * G) return;
+    const int h = item / G, g = item % G, tid = threadIdx.x;
+    const int j0 = g * S, n = min(S, L - j0);
+    if (tid < 256) {
+        uint32_t c = 0;
+        for (int w = 0; w < G; ++w) c += ws.hist0[((size_t)h * G + w) * 256 + tid];
+        tot0[tid] = c;
+    }
+    for (int b = tid; b < kRBins * kRCopies; b += kMT) hist[b] = 0u;
+    __syncthreads();
+    uint32_t k1;
+    const uint32_t b0 = find_bin_from_top<256, 1, kMT>(tot0, (uint32_t)Bp, &k1, scan_lds, s_res);
+    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
+    const uint32_t copy = tid & (kRCopies - 1);
+    uint32_t kv[kMKpt];
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        kv[q] = i < n ? kg[i] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n && (kv[q] >> 24) == b0) atomicAdd(&hist[((kv[q] >> 12) & (kRBins - 1)) * kRCopies + copy], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < kRBins; b += kMT) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int cp = 0; cp < kRCopies; ++cp) c += hist[b * kRCopies + cp];
+        if (c) atomicAdd(&ws.h1[(size_t)h * kRBins + b], c);
+    }
+    if (g == 0 && tid == 0) {
+        ws.state[h * 4 + 0] = b0;
+        ws.state[h * 4 + 1] = k1;
+    }
+}
+
+__global__ __launch_bounds__(kMT) void msel_round2_kernel(int H, int L, int G, int S, MselWs ws) {
+    __shared__ uint32_t hist[kRBins * kRCopies];
+    __shared__ uint32_t scan_lds[kMWaves];
+    __shared__ uint32_t s_res[2];
+    const int item = xcd_item((int)(gridDim.x / 8u));
+    if (item >= H * G) return;
+    const int h = item / G, g = item % G, tid = threadIdx.x;
+    const int j0 = g * S, n = min(S, L - j0);
+    const uint32_t b0 = ws.state[h * 4 + 0], k1 = ws.state[h * 4 + 1];
+    for (int b = tid; b < kRBins; b += kMT) hist[b] = ws.h1[(size_t)h * kRBins + b];
+    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
+    uint32_t kv[kMKpt];
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        kv[q] = i < n ? kg[i] : 0u;
+    }
+    __syncthreads();
+    uint32_t k2;
+    const uint32_t b1 = find_bin_from_top<kRBins, 1, kMT>(hist, k1, &k2, scan_lds, s_res);
+    const uint32_t pre2 = (b0 << 12) | b1;  // top 20 bits of the threshold
+    for (int b = tid; b < kRBins * kRCopies; b += kMT) hist[b] = 0u;
+    __syncthreads();
+    const uint32_t copy = tid & (kRCopies - 1);
+    uint32_t above = 0;
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n) {
+            const uint32_t p = kv[q] >> 12;
+            if (p == pre2) atomicAdd(&hist[(kv[q] & (kRBins - 1)) * kRCopies + copy], 1u);
+            above += p > pre2;
+        }
+    }
+    __syncthreads();
+    // thread t owns bins 4095 - (8t + i), i = 0..7 (descending): suffix counts
+    constexpr int kPer = kRBins / kMT;
+    uint32_t cnt[kPer], mine = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = kRBins - 1 - (tid * kPer + i);
+        uint32_t c = 0;
+#pragma unroll
+        for (int cp = 0; cp < kRCopies; ++cp) c += hist[b * kRCopies + cp];
+        cnt[i] = c;
+        mine += c;
+    }
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan<kMT>(mine, scan_lds, &tot);
+    uint32_t* cum = ws.cum2 + ((size_t)h * G + g) * kCum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = kRBins - 1 - (tid * kPer + i);
+        run += cnt[i];
+        cum[b] = run;  // keys matching the prefix with low 12 bits >= b
+        if (cnt[i]) atomicAdd(&ws.h2[(size_t)h * kRBins + b], cnt[i]);
+    }
+    if (tid == 0) cum[kRBins] = 0u;
+    const uint32_t above_all = block_exclusive_scan<kMT>(above, scan_lds, &tot);
+    (void)above_all;
+    if (tid == 0) ws.gt20[(size_t)h * G + g] = tot;
+    if (g == 0 && tid == 0) {
+        ws.state[h * 4 + 2] = b1;
+        ws.state[h * 4 + 3] = k2;
+    }
+}
+
+__global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, int S, int Bp, MselWs ws,
+                                                           int32_t* __restrict__ idx_out) {
+    __shared__ uint32_t hist[kRBins];
+    __shared__ __align__(16) uint32_t kt[kMMaxKeys];
+    __shared__ uint32_t scan_lds[kMWaves];
+    __shared__ uint32_t s_res[2];
+    const int item = xcd_item((int)(gridDim.x / 8u));
+    if (item >= H * G) return;
+    const int h = item / G, g = item % G, tid = threadIdx.x;
+    const int j0 = g * S, n = min(S, L - j0);
+    const uint32_t b0 = ws.state[h * 4 + 0], b1 = ws.state[h * 4 + 2], k2 = ws.state[h * 4 + 3];
+    for (int b = tid; b < kRBins; b += kMT) hist[b] = ws.h2[(size_t)h * kRBins + b];
+    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n) kt[i] = kg[i];
+    }
+    __syncthreads();
+    uint32_t q;
+    const uint32_t b2 = find_bin_from_top<kRBins, 1, kMT>(hist, k2, &q, scan_lds, s_res);
+    const uint32_t T = (b0 << 24) | (b1 << 12) | b2;  // the B'-th largest key; q of the keys equal to T fit
+    // keys above T and equal to T in the earlier workgroups of the head
+    uint32_t gt_p = 0, eq_p = 0;
+    for (int w = tid; w < g; w += kMT) {
+        const uint32_t* cum = ws.cum2 + ((size_t)h * G + w) * kCum;
+        const uint32_t hi = cum[b2 + 1];
+        gt_p += ws.gt20[(size_t)h * G + w] + hi;
+        eq_p += cum[b2] - hi;
+    }
+    uint32_t gt_before, eq_before;
+    (void)block_exclusive_scan<kMT>(gt_p, scan_lds, &gt_before);
+    (void)block_exclusive_scan<kMT>(eq_p, scan_lds, &eq_before);
+    // this thread's consecutive keys, in token order
+    const int x0 = tid * kMKpt;
+    uint32_t kv[kMKpt];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < kMKpt; ++i) {
+        kv[i] = x0 + i < n ? kt[x0 + i] : 0u;
+        ngt += (x0 + i < n && kv[i] > T);
+        neq += (x0 + i < n && kv[i] == T);
+    }
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan<kMT>(ngt | (neq << 16), scan_lds, &tot);  // also orders kt's reuse
+    const uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
+    const uint32_t tot_gt = tot & 0xffffu, tot_eq = tot >> 16;
+    const uint32_t eq_kept_b = min(eq_before + eq_b, q) - min(eq_before, q);
+    const uint32_t tot_sel = tot_gt + min(eq_before + tot_eq, q) - min(eq_before, q);
+    uint32_t eq_rank = eq_before + eq_b;
+    uint32_t pos = gt_b + eq_kept_b;
+#pragma unroll
+    for (int i = 0; i < kMKpt; ++i) {
+        if (x0 + i < n) {
+            bool keep = kv[i] > T;
+            if (kv[i] == T) { keep = eq_rank < q; ++eq_rank; }
+            if (keep) kt[pos++] = (uint32_t)(j0 + x0 + i);
+        }
+    }
+    __syncthreads();
+    const uint32_t base = gt_before + min(eq_before, q);
+    int32_t* idx_h = idx_out + (size_t)h * Bp;
+    for (uint32_t i = tid; i < tot_sel; i += kMT)
+        if (base + i < (uint32_t)Bp) idx_h[base + i] = (int32_t)kt[i];  // always true when the counts agree
+}
+
 // K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
 // kRowBytes/16 lanes, kGatherRows output rows per block.  Rows are read and
 // written once, with non-temporal accesses.  With pos_out, the tokens'
@@ -488,7 +842,67 @@ hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K
     return hipGetLastError();
 }
 
+struct MselPlan {
+    int G, S;  // workgroups per head and keys per workgroup; G == 0: one workgroup per head
+};
+
+// Heads of one chunk keep the one-workgroup kernel (its keys stay in LDS
+// between the passes).  Longer heads split into G workgroups of S <= 8192
+// consecutive keys: at least 1024 keys each, and enough workgroups for about
+// two per compute unit of a 256-CU device when the heads are few.
+MselPlan msel_plan(int H, int L) {
+    if (L <= kChunk) return MselPlan{0, 0};
+    long long G = (L + kMMaxKeys - 1) / kMMaxKeys;
+    const long long g_fill = (512 + H - 1) / H, g_max = (L + 1023) / 1024;
+    const long long g_want = g_fill < g_max ? g_fill : g_max;
+    if (g_want > G) G = g_want;
+    const int S = (int)((L + G - 1) / G);
+    return MselPlan{(int)((L + S - 1) / S), S};  // every workgroup non-empty
+}
+
+constexpr size_t kWsAlign = 256;
+size_t ws_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Layout of the selection workspace: keys, then (split plans only) the
+// histograms, counts and per-head state.  Offsets in bytes; [7] = total.
+void msel_offsets(int H, int L, const MselPlan& mp, size_t (&o)[8]) {
+    const size_t h = (size_t)H, G = (size_t)mp.G;
+    size_t x = 0;
+    o[0] = x; x = ws_up(x + h * (size_t)L * 4);  // keys
+    if (mp.G > 0) {
+        o[1] = x; x = ws_up(x + h * G * 256 * 4);
+        o[2] = x; x = ws_up(x + h * kRBins * 4);
+        o[3] = x; x = ws_up(x + h * kRBins * 4);
+        o[4] = x; x = ws_up(x + h * G * 4);
+        o[5] = x; x = ws_up(x + h * G * kCum * 4);
+        o[6] = x; x = ws_up(x + h * 4 * 4);
+    } else {
+        for (int i = 1; i < 7; ++i) o[i] = x;
+    }
+    o[7] = x;
+}
+
+MselWs msel_carve(void* base, int H, int L, const MselPlan& mp) {
+    size_t o[8];
+    msel_offsets(H, L, mp, o);
+    auto at = [&](int i) { return reinterpret_cast<uint32_t*>(static_cast<char*>(base) + o[i]); };
+    return MselWs{at(0), at(1), at(2), at(3), at(4), at(5), at(6)};
+}
+
 }  // namespace
+
+size_t sel_ws_bytes(int H, int L) {
+    const MselPlan mp = msel_plan(H, L);
+    size_t o[8];
+    msel_offsets(H, L, mp, o);
+    return o[7];
+}
+
+bool sel_grid_fits(int H, int L) {
+    const MselPlan mp = msel_plan(H, L);
+    const long long wgs = ((long long)H * mp.G + 7) / 8 * 8;
+    return wgs * kMT < (1LL << 32);
+}
 
 hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const float2* red_part, int nbr, float lam,
                            int w, float* score_out, float* imp_pooled_out, float* red_out, uint32_t* keys, int H,
@@ -498,6 +912,21 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
     // Heads of several chunks keep the 4-byte loads: measured on the
     // long-video shape, the 16-byte form was slower there (171.0 against
     // 166.5 us), against 27.0 -> 26.0 us on the MAGI-like shape.
+    const MselPlan mp = msel_plan(H, L);
+    if (mp.G > 0) {
+        const MselWs ws = msel_carve(keys, H, L, mp);
+        const dim3 grid((unsigned)(((long long)H * mp.G + 7) / 8 * 8));
+        if (r != nullptr)
+            hipLaunchKernelGGL(msel_keys_kernel<true>, grid, dim3(kMT), 0, s, src, nsrc, r, red_part, nbr, lam,
+                               (w - 1) / 2, score_out, imp_pooled_out, red_out, H, L, mp.G, mp.S, ws);
+        else
+            hipLaunchKernelGGL(msel_keys_kernel<false>, grid, dim3(kMT), 0, s, src, 1, nullptr, nullptr, 0, 0.f, 0,
+                               nullptr, nullptr, nullptr, H, L, mp.G, mp.S, ws);
+        hipLaunchKernelGGL(msel_round1_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws);
+        hipLaunchKernelGGL(msel_round2_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, ws);
+        hipLaunchKernelGGL(msel_compact_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws, idx_out);
+        return hipGetLastError();
+    }
     const bool vec = L <= kChunk && L % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
                      (r == nullptr || (reinterpret_cast<uintptr_t>(r) & 15) == 0);
     if (r != nullptr) {

@@ -164,8 +164,17 @@ def test_redundancy_stage(fc):
     assert float(r[0, 7]) == 0.0
 
 
+# Heads of more than 18432 scores take the selection split over several
+# workgroups per head: just above that size, many exact ties, B = 1,
+# B = L - 1, B = L, many heads, and one head of 4.5M scores (more workgroups
+# per head than threads in one, so the compaction loops over the earlier ones).
+SPLIT_CASES = [(1, 18433, 9000, 0), (3, 129600, 32400, 3), (24, 40000, 1, 0), (5, 30000, 29999, 2),
+               (2, 20000, 20000, 0), (1, 4_500_000, 1_000_000, 20), (40, 46800, 15600, 0)]
+
+
 @pytest.mark.parametrize("H,L,B,levels", [(1, 10, 3, 0), (4, 5000, 1234, 0), (3, 5000, 2500, 7), (2, 70000, 20000, 50),
-                                          (2, 4096, 4096, 3), (2, 100, 400, 0), (3, 2049, 1, 2), (1, 3, 2, 1)])
+                                          (2, 4096, 4096, 3), (2, 100, 400, 0), (3, 2049, 1, 2), (1, 3, 2, 1)]
+                         + SPLIT_CASES)
 def test_topb_select_exact(fc, H, L, B, levels):
     s = synth.random_scores(H, L, seed=H * 1000 + L, n_levels=levels)
     if levels == 0 and L >= 10:

@@ -45,6 +45,15 @@ def kv_configs(n, seed):
     return out
 
 
+# shapes whose heads exceed one 18432-key chunk (the split selection), small
+# query counts so the oracle stays fast
+SPLIT = [
+    ("bf16", 128, 2, 40, 18433, 6000, 7, 0.5, 0.0, 951),
+    ("bf16", 64, 3, 17, 50000, 25001, 9, 0.3, 0.0, 952),
+    ("f32", 128, 1, 9, 37000, 36999, 129, 0.7, 0.0, 953),
+    ("bf16", 128, 5, 33, 24000, 1, 1, 0.0, 0.0, 954),
+]
+
 CORNERS = [
     # one query and one key; one key, budget above it; every token kept with
     # lambda = 1; lambda = 0 with a wide window; a 1-wide window at B = 1
@@ -56,7 +65,7 @@ CORNERS = [
 ]
 
 
-@pytest.mark.parametrize("dtype,d,H,Lq,Lk,B,w,lam,scale,seed", kv_configs(16, 2026) + CORNERS)
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk,B,w,lam,scale,seed", kv_configs(16, 2026) + CORNERS + SPLIT)
 def test_random_compress(fc, dtype, d, H, Lq, Lk, B, w, lam, scale, seed):
     say(f"case: {dtype} d={d} H={H} Lq={Lq} Lk={Lk} B={B} w={w} lambda={lam} scale={scale} seed={seed}")
     Q, K, V = synth.random_kv(H, Lq, Lk, d, dtype, seed=seed)
