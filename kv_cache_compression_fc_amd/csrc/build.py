@@ -53,5 +53,27 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+MICROBENCH = os.path.join(HERE, "microbench")
+
+
+def build_microbench(verbose: bool = False) -> list:
+    """Stand-alone measurement programs (not part of the library): each
+    ``microbench/*.hip`` becomes an executable in ``csrc/_build/``."""
+    os.makedirs(BUILD, exist_ok=True)
+    exes = []
+    for src in sorted(glob.glob(os.path.join(MICROBENCH, "*.hip"))):
+        exe = os.path.join(BUILD, os.path.basename(src)[:-4])
+        cmd = [HIPCC, *[f for f in CFLAGS if f != "-fPIC"], src, "-o", exe]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src}")
+        exes.append(exe)
+    return exes
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_microbench(verbose=True)
