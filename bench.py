@@ -4,22 +4,23 @@
 One step = one pass of the whole path over one batch of synthetic inputs
 already resident in HBM (the two parts are independent and run on two
 streams):
-  * fc_kv_compress on the MAGI-like workload (24 heads, d=128, 3600 denoising
-    queries, 18000 clean keys, keep 7200 per head, lambda 0.5, pool window 7,
-    bf16): importance (two MFMA passes), redundancy, pool + score + top-B,
-    K/V compaction;
+  * fc_kv_compress on the long-video workload (24 heads, d=128, 8100
+    denoising queries, 129600 clean keys = 16 chunks of 4 x 45 x 45 tokens,
+    keep 32400 per head, lambda 0.5, pool window 7, bf16; the smooth-field
+    keys of the generator with frames 48-63 copied from frames 16-31):
+    importance (two MFMA passes, the redundancy fused into them), pool +
+    score + top-B, K/V compaction;
   * fc_chunk_rel_l1_decide on 16 concurrent chunks of 64x8x90x160 bf16
     latents (steady state, all chunks active at staggered local steps).
 
-Beside the step it times a MAGI-like run of the KV cache manager
-(fc_cache_commit: chunks of 3600 tokens into a budget of 7200 per head) and
-reports it under "cache".
+Beside the step it times the stages on the same inputs, the lambda sweep
+{0.3, 0.5, 0.7}, the MAGI-like and SkyReels-like compressions, a MAGI-like run
+of the KV cache manager, and the oracle on the host cores (CPU baseline).
 
 Prints one JSON line.  `value` is clean-KV token-heads scored and selected per
-second over whole steps (the chunk decision included).  The dominant kernel
-(importance pass 1) is timed on its own with HIP events on the stream it runs
-on, for the roofline entry; the oracle is timed on the host cores on a bounded
-sample for the CPU baseline.
+second over whole steps (the chunk decision included).  The roofline entry is
+the importance stage (its three launches, timed with HIP events on the stream
+they run on), with Q K^T counted once over both passes.
 """
 from __future__ import annotations
 
@@ -38,16 +39,21 @@ sys.path.insert(0, ROOT)
 METRIC = "clean KV tokens scored+selected/sec/head; L1 GB/s; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "imp_lse_magi_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_compression_fc_amd", "csrc", "importance.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "importance_long_traffic.json")
+CSRC = os.path.join(ROOT, "kv_cache_compression_fc_amd", "csrc")
+TRAFFIC_SOURCES = ("importance.hip", "red_rows.hpp", "common.hpp")
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash() -> str:
+    """Hash of the sources of the importance stage's kernels."""
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def time_events(fn, reps: int) -> float:
@@ -62,30 +68,6 @@ def time_events(fn, reps: int) -> float:
     e.record()
     e.synchronize()
     return s.elapsed_time(e) / reps
-
-
-def time_graph(fn, reps: int):
-    """Average ms per call with the calls captured in a HIP graph (no host
-    launch gaps between small kernels); falls back to eager event timing."""
-    import torch
-    try:
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        g.replay()
-        e.record()
-        e.synchronize()
-        return s.elapsed_time(e) / reps, "graph"
-    except Exception as exc:  # pragma: no cover - capture not available
-        log(f"graph capture failed ({exc}); eager timing")
-        return time_events(fn, reps), "eager"
 
 
 def time_cold(fn, reps: int, scratch):
@@ -119,38 +101,53 @@ def time_cold(fn, reps: int, scratch):
     return sum(s.elapsed_time(e) for s, e in evs) / reps, how
 
 
+def workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_info() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            return next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
 def cpu_baseline(cfg, ccfg, min_seconds: float):
-    """The oracle (never tuned) on whole steps of the same workload: all heads
-    of the KV compression and the decision for every chunk, repeated until
-    about min_seconds of host time have passed."""
+    """The oracle (never tuned) on a bounded sample of the same step: the
+    whole fp64 compression of sampled heads of the long-video workload (the
+    generator's values; importance in C + OpenMP, the rest in numpy), and the
+    relative-L1 decision of all 16 chunks (numpy).  Heads are independent and
+    equally sized, so a step costs H x (mean time per head) + the decision."""
     import oracle
     from kv_cache_compression_fc_amd import synth
-    Q, K, V = synth.kv_inputs(cfg, seed=0)
     tr = synth.ChunkTrajectory(ccfg, seed=0)
     xt, xtm1, steps = tr.pair(ccfg.n_chunks - 1)
     offs = [i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)]
+    t0 = time.perf_counter()
+    l1 = oracle.chunk_l1_rel(xt, xtm1, offs)
     f = [0.0] * ccfg.n_chunks
-    reps, t_total = 0, 0.0
-    while reps == 0 or t_total < min_seconds:
+    for i, n in enumerate(steps):
+        if n >= 0:
+            _, f[i] = oracle.decide(n, f[i], l1[i], ccfg.m, ccfg.eps[0])
+    t_dec = time.perf_counter() - t0
+    del xt, xtm1, tr
+    head_times = []
+    h = 0
+    while not head_times or sum(head_times) + t_dec < min_seconds:
+        Q, K, V = synth.kv_inputs(cfg, seed=0, heads=[h])
         t0 = time.perf_counter()
-        oracle.kv_compress(Q, K, V, cfg.B, cfg.lam[0], cfg.w)
-        l1 = oracle.chunk_l1_rel(xt, xtm1, offs)
-        for i, n in enumerate(steps):
-            if n >= 0:
-                _, f[i] = oracle.decide(n, f[i], l1[i], ccfg.m, ccfg.eps[0])
-        t_total += time.perf_counter() - t0
-        reps += 1
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as fh:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return {"value": cfg.H * cfg.Lk * reps / t_total, "unit": "token-heads/s", "cores": oracle.num_threads(),
-            "cpu": cpu, "kind": "oracle", "seconds": t_total,
-            "sample": f"{reps} whole step(s) of the same workload: fp64 compression of all {cfg.H} heads "
-                      f"(L_q={cfg.Lq}, L_k={cfg.Lk}, C + OpenMP importance, numpy rest) and the relative-L1 "
-                      f"decision of {ccfg.n_chunks} chunks (numpy)"}
+        oracle.kv_compress(Q, K, V, cfg.B, 0.5, cfg.w)
+        head_times.append(time.perf_counter() - t0)
+        h = (h + 1) % cfg.H
+    t_step = cfg.H * statistics.mean(head_times) + t_dec
+    return {"value": cfg.H * cfg.Lk / t_step, "unit": "token-heads/s", "cores": oracle.num_threads(),
+            "cpu": cpu_info(), "kind": "oracle", "seconds": sum(head_times) + t_dec,
+            "step_seconds_estimated": t_step,
+            "sample": f"{len(head_times)} of {cfg.H} long-video heads compressed whole in fp64 "
+                      f"(L_q={cfg.Lq}, L_k={cfg.Lk}, B={cfg.B}, lambda 0.5; mean {statistics.mean(head_times):.2f} s "
+                      f"per head, scaled by H={cfg.H}) plus the relative-L1 decision of {ccfg.n_chunks} chunks "
+                      f"({t_dec:.2f} s)"}
 
 
 def cache_run(fc, synth, dev, reps: int):
@@ -197,32 +194,39 @@ def cache_run(fc, synth, dev, reps: int):
 
 
 def other_shapes(fc, synth, dev, reps: int):
-    """fc_kv_compress alone on the SkyReels-like and long-video shapes (all
-    heads), inputs drawn on the device (seeded N(0,1) bf16; their parity at
-    these sizes is the tests' business): token-heads/s and the importance
-    rate."""
+    """fc_kv_compress alone on the MAGI-like shape (the generator's values)
+    and the SkyReels-like shape (seeded N(0,1) bf16 drawn on the device; its
+    parity at this size is the tests' business): token-heads/s and the
+    importance rate."""
     import torch
     out = {}
     g = torch.Generator(device=dev)
     g.manual_seed(7)
-    for name in ("skyreels", "long"):
+    for name in ("magi", "skyreels"):
         cfg = synth.KV_CONFIGS[name]
         H, Lq, Lk, d, B = cfg.H, cfg.Lq, cfg.Lk, cfg.d, cfg.B
-        Q = torch.randn((H, Lq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        K = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        V = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        if name == "magi":
+            Q, K, V = (x.to(dev) for x in synth.kv_inputs(cfg, seed=0, workers=workers()))
+            data = "generator (smooth-field keys)"
+        else:
+            Q = torch.randn((H, Lq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            K = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            V = torch.randn((H, Lk, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            data = "device-seeded N(0,1) bf16"
         lam = 0.5
         p = fc.kv_params(Q, K, B, lam, cfg.w)
         ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=dev)
         o = {"K_out": torch.empty((H, B, d), dtype=K.dtype, device=dev),
              "V_out": torch.empty((H, B, d), dtype=V.dtype, device=dev),
              "idx": torch.empty((H, B), dtype=torch.int32, device=dev)}
-        t = time_events(lambda: fc.fc_kv_compress(Q, K, V, B, lam, cfg.w, out=o, workspace=ws), max(2, reps // 2))
-        flops = 2 * 2.0 * H * Lq * Lk * d   # both importance passes
+        t = time_events(lambda: fc.fc_kv_compress(Q, K, V, B, lam, cfg.w, out=o, workspace=ws), reps)
+        t_imp = time_events(lambda: fc.fc_kv_importance_redundancy(Q, K, workspace=ws), reps)
+        flops = 2.0 * H * Lq * Lk * d   # Q K^T once
         out[name] = {"H": H, "L_q": Lq, "L_k": Lk, "B_budget": B, "compress_ms": t,
                      "token_heads_per_s": H * Lk / (t * 1e-3), "tokens_per_s_per_head": Lk / (t * 1e-3),
-                     "importance_executed_tflops_upper": flops / (t * 1e-3) / 1e12,
-                     "data": "device-seeded N(0,1) bf16"}
+                     "importance_stage_ms": t_imp,
+                     "importance_algorithmic_tflops": flops / (t_imp * 1e-3) / 1e12,
+                     "select_gather_in_compress_ms": t - t_imp, "data": data}
         del Q, K, V, ws, o
         torch.cuda.empty_cache()
     return out
@@ -234,13 +238,15 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="minimum host time of the CPU-baseline (oracle) leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cache", action="store_true",
-                    help="skip the KV-cache run and the SkyReels-like / long-video compressions")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other shapes and the KV-cache run")
+    ap.add_argument("--profile-importance", type=int, default=0, metavar="N",
+                    help="only run the importance stage N times on the long-video inputs (for counter runs)")
     ap.add_argument("--loop-lse", type=float, default=0.0, metavar="SECONDS",
-                    help="only run importance pass 1 on the MAGI-like shape back to back for SECONDS "
+                    help="only run importance pass 1 on the long-video shape back to back for SECONDS "
                          "(to read the board's power and clocks meanwhile)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
@@ -269,40 +275,52 @@ def main() -> int:
         print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 3}), flush=True)
         return 0
 
-    cfg = synth.KV_CONFIGS["magi"]
+    cfg = synth.KV_CONFIGS["long"]
     ccfg = synth.CHUNK_CONFIGS["scale"]
+    H, Lq, Lk, d, B, w = cfg.H, cfg.Lq, cfg.Lk, cfg.d, cfg.B, cfg.w
+    lam = 0.5
+    Bp = min(B, Lk)
+    log(f"generating inputs: {cfg.name} KV workload ({workers()} threads)")
+    t0 = time.perf_counter()
+    Q, K, V = synth.kv_inputs(cfg, seed=0, workers=workers())
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    del Q, K, V
+    log(f"  {time.perf_counter() - t0:.1f} s")
+    p = fc.kv_params(Qd, Kd, B, lam, w)
+    ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=dev)
+
+    if args.profile_importance > 0:
+        imp = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+        r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+        for _ in range(args.profile_importance):
+            fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_importance_calls": args.profile_importance}), flush=True)
+        return 0
     if args.loop_lse > 0:
-        Q, K, _ = synth.kv_inputs(cfg, seed=0)
-        Qd, Kd = Q.to(dev), K.to(dev)
-        lse = fc.fc_kv_importance_lse(Qd, Kd)
+        lse = fc.fc_kv_importance_lse(Qd, Kd, workspace=ws)
         torch.cuda.synchronize()
         log("loop start")
         t0, calls = time.perf_counter(), 0
         while time.perf_counter() - t0 < args.loop_lse:
-            for _ in range(50):
-                fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse)
+            for _ in range(5):
+                fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws)
             torch.cuda.synchronize()
-            calls += 50
+            calls += 5
         dt = time.perf_counter() - t0
         print(json.dumps({"loop_lse_calls": calls, "ms_per_call": 1e3 * dt / calls}), flush=True)
         return 0
-    log(f"generating inputs: {cfg.name} KV workload and {ccfg.n_chunks} chunk states")
-    Q, K, V = synth.kv_inputs(cfg, seed=0)
-    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
-    del Q, K, V
+
+    log(f"generating {ccfg.n_chunks} chunk states")
     tr = synth.ChunkTrajectory(ccfg, seed=0)
     g_steady = ccfg.n_chunks - 1  # every chunk active, local steps 15..0
     xt, xtm1, steps = tr.pair(g_steady)
     xt_d, xtm1_d = xt.to(dev), xtm1.to(dev)
     del xt, xtm1, tr
-    dec = fc.ChunkDecider([i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)], ccfg.m, ccfg.eps[0],
-                          torch.bfloat16, dev)
+    offs_c = [i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)]
+    dec = fc.ChunkDecider(offs_c, ccfg.m, ccfg.eps[0], torch.bfloat16, dev)
     dec.step.copy_(torch.tensor(steps, dtype=torch.int32))
 
-    H, Lq, Lk, d, B = cfg.H, cfg.Lq, cfg.Lk, cfg.d, cfg.B
-    Bp = min(B, Lk)
-    p = fc.kv_params(Qd, Kd, B, cfg.lam[0], cfg.w)
-    ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=dev)
     out = {"K_out": torch.empty((H, Bp, d), dtype=Kd.dtype, device=dev),
            "V_out": torch.empty((H, Bp, d), dtype=Vd.dtype, device=dev),
            "idx": torch.empty((H, Bp), dtype=torch.int32, device=dev)}
@@ -312,14 +330,14 @@ def main() -> int:
     # forked at the start of the step and joined at its end, so its HBM
     # traffic overlaps the compression's compute.
     side = torch.cuda.Stream(device=dev)
-    main = torch.cuda.current_stream()
+    main_s = torch.cuda.current_stream()
 
     def step():
-        side.wait_stream(main)
+        side.wait_stream(main_s)
         with torch.cuda.stream(side):
             dec.decide(xt_d, xtm1_d, stream=side)
-        fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws)
-        main.wait_stream(side)
+        fc.fc_kv_compress(Qd, Kd, Vd, B, lam, w, out=out, workspace=ws)
+        main_s.wait_stream(side)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -338,27 +356,35 @@ def main() -> int:
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     log(f"ms/step {ms_per_step:.4f} (wall {1e3 * wall / args.steps:.4f})")
 
-    # Per-stage timings (same inputs, same stream, HIP events).
+    # Stages on the same inputs, same stream, HIP events.
     reps = args.kernel_reps
-    lse = torch.empty((H, Lq), dtype=torch.float32, device=dev)
     imp = torch.empty((H, Lk), dtype=torch.float32, device=dev)
     r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
-    fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws)
+    lse = torch.empty((H, Lq), dtype=torch.float32, device=dev)
+    # the importance stage exactly as the step runs it: pass 1 with redundancy
+    # pass A, the merge, pass 2 with redundancy pass B
+    t_imp = time_events(lambda: fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws), reps)
+    # the two passes alone (without the redundancy), for the per-pass rates
     t_lse = time_events(lambda: fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws), reps)
     t_colsum = time_events(lambda: fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp, workspace=ws), reps)
-    t_red, how_red = time_graph(lambda: fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws), reps)
-    t_sel, how_sel = time_graph(lambda: fc.fc_kv_select(imp, r, B, cfg.lam[0], cfg.w, Kd, Vd, want_scores=False,
-                                                        workspace=ws), reps)
-    t_compress = time_events(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, cfg.lam[0], cfg.w, out=out, workspace=ws),
-                             reps)
+    fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws)
+    t_red = time_events(lambda: fc.fc_kv_redundancy(Kd, r_out=torch.empty_like(r), workspace=ws), reps)
+    t_sel = time_events(lambda: fc.fc_kv_select(imp, r, B, lam, w, Kd, Vd, want_scores=False, workspace=ws), reps)
+    t_sel_idx = time_events(lambda: fc.fc_kv_select(imp, r, B, lam, w, want_scores=False, workspace=ws), reps)
+    sweep = {}
+    for lam_s in cfg.lam:
+        t_c = time_events(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, lam_s, w, out=out, workspace=ws), reps)
+        sweep[str(lam_s)] = {"compress_ms": t_c, "token_heads_per_s": H * Lk / (t_c * 1e-3)}
+    t_compress = sweep[str(lam)]["compress_ms"]
     t_l1 = time_events(lambda: dec.decide(xt_d, xtm1_d), reps)
-    # the other two decision rules on the same pair of states: one decision
-    # for all chunks (uniform), and the history-guided refresh per chunk
     n_ch = ccfg.n_chunks
-    offs_c = [i * ccfg.chunk_elems for i in range(n_ch + 1)]
     p_pol = fc.fc_l1_params(n_ch, ccfg.m, ccfg.eps[0], fc.FC_BF16)
-    ws_pol = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p_pol, offs_c), dtype=torch.uint8, device=dev)
     cstep = torch.tensor(steps, dtype=torch.int32, device=dev)
+    st_na, f_na = cstep.clone(), torch.zeros(n_ch, device=dev)
+    rec_na = torch.zeros(n_ch, dtype=torch.uint8, device=dev)
+    t_noalloc = time_events(lambda: fc.fc_chunk_rel_l1_decide_noalloc(p_pol, offs_c, xt_d, xtm1_d, st_na, f_na, rec_na),
+                            reps)
+    ws_pol = torch.empty(fc.fc_chunk_rel_l1_workspace_bytes(p_pol, offs_c), dtype=torch.uint8, device=dev)
     gstep = torch.zeros(1, dtype=torch.int32, device=dev)
     f_u, l1_u = torch.zeros(1, device=dev), torch.zeros(1, device=dev)
     rec_u = torch.zeros(n_ch, dtype=torch.uint8, device=dev)
@@ -371,37 +397,41 @@ def main() -> int:
                                                              dev_h, ws_pol), reps)
     # the HBM-bound stages again with the MALL flushed before every call
     scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB
-    t_red_c, _ = time_cold(lambda: fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws), reps, scratch)
-    t_sel_c, _ = time_cold(lambda: fc.fc_kv_select(imp, r, B, cfg.lam[0], cfg.w, Kd, Vd, want_scores=False,
-                                                   workspace=ws), reps, scratch)
-    t_l1_c, _ = time_cold(lambda: dec.decide(xt_d, xtm1_d), reps, scratch)
+    t_red_c, _ = time_cold(lambda: fc.fc_kv_redundancy(Kd, r_out=torch.empty_like(r), workspace=ws), reps, scratch)
+    t_sel_c, _ = time_cold(lambda: fc.fc_kv_select(imp, r, B, lam, w, Kd, Vd, want_scores=False, workspace=ws),
+                           reps, scratch)
+    t_l1_c, how_cold = time_cold(lambda: dec.decide(xt_d, xtm1_d), reps, scratch)
     del scratch
     # the fused variant: Euler update X_{t-1} = X_t + v dt and the decision in
     # one pass, in place, on the same 16 chunks (velocity: the path's own)
     v_d = synth.ChunkTrajectory(ccfg, seed=0).velocity().to(dev)
     x_work = xt_d.clone()
     dts = torch.full((ccfg.n_chunks,), -1e-4, dtype=torch.float32, device=dev)
-    dec_fused = fc.ChunkDecider([i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)], ccfg.m, ccfg.eps[0],
-                                torch.bfloat16, dev)
+    dec_fused = fc.ChunkDecider(offs_c, ccfg.m, ccfg.eps[0], torch.bfloat16, dev)
     dec_fused.step.copy_(torch.tensor(steps, dtype=torch.int32))   # every chunk active; the counters advance
     t_fused = time_events(lambda: dec_fused.euler_step(x_work, v_d, dts, x_work), reps)
     del v_d, x_work
     torch.cuda.synchronize()
 
-    mfma_flops = 2.0 * H * Lq * Lk * d            # one Q K^T product (each pass executes one)
+    qk_flops = 2.0 * H * Lq * Lk * d              # one Q K^T product (the method's own work)
     red_bytes = H * Lk * (d * 2 + 4)              # read K once, write r
     sel_bytes = 8 * H * Lk + 4 * H * Bp + 2 * 2 * H * Bp * d * 2   # imp + r, idx, K/V rows read + written
     l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
     fused_bytes = 3 * ccfg.n_chunks * ccfg.chunk_elems * 2          # X_t and v read, X_{t-1} written
-    lse_tflops = mfma_flops / (t_lse * 1e-3) / 1e12
+    imp_tflops = qk_flops / (t_imp * 1e-3) / 1e12
+    sel_in_step = t_compress - t_imp
     stages = {
-        "importance_lse_ms": t_lse, "importance_lse_tflops": lse_tflops,
-        "importance_colsum_ms": t_colsum, "importance_colsum_tflops": mfma_flops / (t_colsum * 1e-3) / 1e12,
-        # Q K^T counted once over both passes (the two-pass method executes it twice)
-        "importance_algorithmic_tflops": mfma_flops / ((t_lse + t_colsum) * 1e-3) / 1e12,
-        "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
+        "importance_stage_ms": t_imp, "importance_algorithmic_tflops": imp_tflops,
+        "importance_executed_tflops": 2 * imp_tflops,
+        "importance_pass1_ms": t_lse, "importance_pass1_tflops": qk_flops / (t_lse * 1e-3) / 1e12,
+        "importance_pass2_ms": t_colsum, "importance_pass2_tflops": qk_flops / (t_colsum * 1e-3) / 1e12,
+        "select_gather_in_compress_ms": sel_in_step,
+        "select_gather_in_compress_gbps": sel_bytes / (sel_in_step * 1e-3) / 1e9,
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
+        "select_indices_only_ms": t_sel_idx,
+        "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
+        "chunk_l1_noalloc_ms": t_noalloc, "chunk_l1_noalloc_gbps": l1_bytes / (t_noalloc * 1e-3) / 1e9,
         "euler_l1_fused_ms": t_fused, "euler_l1_fused_gbps": fused_bytes / (t_fused * 1e-3) / 1e9,
         "uniform_l1_ms": t_uni, "uniform_l1_gbps": l1_bytes / (t_uni * 1e-3) / 1e9,
         "history_l1_ms": t_hist, "history_l1_gbps": l1_bytes / (t_hist * 1e-3) / 1e9,
@@ -410,29 +440,31 @@ def main() -> int:
             "select_gather_ms": t_sel_c, "select_gather_gbps": sel_bytes / (t_sel_c * 1e-3) / 1e9,
             "chunk_l1_ms": t_l1_c, "chunk_l1_gbps": l1_bytes / (t_l1_c * 1e-3) / 1e9,
         },
-        "timing": f"events; redundancy {how_red}, select {how_sel}; mall_flushed: 512 MB read before each "
-                  f"call, one call per graph replay",
+        "lambda_sweep": sweep,
+        "timing": f"HIP events on the launch stream, {reps} calls each; mall_flushed: 512 MB read before each "
+                  f"call, one call per {how_cold} replay; select_gather includes the redundancy softmax "
+                  f"statistics kernel that fc_kv_compress takes from pass 2 instead",
     }
     for k, v in stages.items():
         log(f"  {k}: {v}")
 
-    others = None
-    if not args.no_cache:
+    others = cache = None
+    if not args.no_extras:
+        del Qd, Kd, Vd, ws, out, imp, r, lse
+        torch.cuda.empty_cache()
         others = other_shapes(fc, synth, dev, reps)
         for k, v in others.items():
             log(f"  {k}: {v}")
-
-    cache = None
-    if not args.no_cache:
         cache = cache_run(fc, synth, dev, reps)
         for k, v in cache.items():
             log(f"  cache {k}: {v}")
 
-    traffic = None
+    traffic = traffic_rec = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("kernel_source_sha256_16") == source_hash(KERNEL_SRC):
-            traffic = rec.get("hbm_bytes_per_launch")
+        if rec.get("kernel_source_sha256_16") == source_hash():
+            traffic = rec.get("hbm_bytes_per_stage")
+            traffic_rec = {k: rec[k] for k in ("per_kernel", "fetch_factor", "write_factor") if k in rec}
 
     result = {
         "metric": METRIC,
@@ -446,26 +478,33 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded smooth-field keys, N(0,1) queries/values; flow-matching chunk trajectories)",
+        "data": "synthetic (seeded smooth-field keys with repeated chunks, N(0,1) queries/values; "
+                "flow-matching chunk trajectories)",
         "config": {
-            "workload": "MAGI-like KV compression + chunk relative-L1 decision",
-            "H": H, "d": d, "L_q": Lq, "L_k": Lk, "B_budget": B, "lambda": cfg.lam[0], "pool_window": cfg.w,
+            "workload": "long-video KV compression + chunk relative-L1 decision",
+            "H": H, "d": d, "L_q": Lq, "L_k": Lk, "B_budget": B, "lambda": lam, "pool_window": w,
+            "duplicated_frames": [list(cfg.dup[1]), "copied from", list(cfg.dup[0])],
             "chunks": ccfg.n_chunks, "chunk_shape": [64, 8, 90, 160], "m": ccfg.m, "eps": ccfg.eps[0],
         },
         "tokens_per_s_per_head": Lk / (ms_per_step * 1e-3),
         "l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "imp_lse_kernel<bf16,128> (importance pass 1)",
-            "bound": "mfma", "achieved": lse_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": lse_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-            "avg_launch_ms": t_lse, "algorithmic_per_launch": mfma_flops,
+            "kernel": "importance stage: imp_lse_kernel (pass 1 + redundancy pass A) + imp_lse_merge_kernel + "
+                      "imp_colsum_kernel (pass 2 + redundancy pass B)",
+            "bound": "mfma", "achieved": imp_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": imp_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "executed_frac": 2 * imp_tflops / PEAK_BF16_TFLOPS,
+            "avg_launch_ms": t_imp, "algorithmic_per_launch": qk_flops,
+            "algorithmic_definition": "2*H*L_q*L_k*d flops: Q K^T counted once; the two-pass method executes it "
+                                      "twice (executed_frac)",
+            "traffic_detail": traffic_rec,
         },
         "stages": stages,
     }
-    if cache is not None:
-        result["cache"] = cache
     if others is not None:
         result["other_shapes"] = others
+    if cache is not None:
+        result["cache"] = cache
     # Context only: the FlowCache page's main table (section on key
     # experimental data) gives whole-video generation times with the models
     # on an A800; they include the transformer forwards this library does not
@@ -476,7 +515,7 @@ def main() -> int:
                                   "SkyReels-V2": {"vanilla": 1540, "flowcache_fast": 230}},
     }
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on whole steps")
+        log("cpu baseline: oracle on a sample of the step")
         result["cpu_baseline"] = cpu_baseline(cfg, ccfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0

@@ -94,9 +94,10 @@ typedef struct {
     fc_dtype dtype;
 } fc_kv_params;
 
-/* Workspace bytes that fc_kv_compress, fc_kv_importance, fc_kv_importance_lse,
- * fc_kv_importance_colsum, fc_kv_redundancy and fc_kv_select need for these
- * parameters (0 if the parameters are invalid). */
+/* Workspace bytes that fc_kv_compress, fc_kv_importance,
+ * fc_kv_importance_redundancy, fc_kv_importance_lse, fc_kv_importance_colsum,
+ * fc_kv_redundancy and fc_kv_select need for these parameters (0 if the
+ * parameters are invalid). */
 size_t fc_kv_compress_workspace_bytes(const fc_kv_params* p);
 
 /*
@@ -138,6 +139,20 @@ fc_status fc_kv_compress(const fc_kv_params* p, const void* Q, const void* K, co
  */
 fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, float* imp_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fc_kv_importance_redundancy -- the first half of fc_kv_compress, with the
+ * same launches: importance pass 1 with the partial sums of the normalised
+ * keys in extra workgroups, the merge, then pass 2, which also forms the
+ * redundancy of the keys it holds:
+ *   imp_out[h][j] as fc_kv_importance writes it (the same bits),
+ *   r_out[h][j]   = (1/L_k) sum_{i != j} khat_i.khat_j  as fc_kv_redundancy
+ *                   defines it (float32 sums in another order).
+ * Q, K device (dtype); imp_out, r_out [H][L_k] f32 device.  Uses p->H, d,
+ * L_q, L_k, softmax_scale, dtype.  Their outputs feed fc_kv_select.
+ */
+fc_status fc_kv_importance_redundancy(const fc_kv_params* p, const void* Q, const void* K, float* imp_out,
+                                      float* r_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fc_kv_importance_lse -- the first of the two passes alone:

@@ -31,7 +31,7 @@ FC_MAX_CHUNKS = 128
 
 EXPORTS = (
     "fc_status_string", "fc_kv_compress_workspace_bytes", "fc_kv_compress", "fc_kv_importance",
-    "fc_kv_importance_lse", "fc_kv_importance_colsum",
+    "fc_kv_importance_lse", "fc_kv_importance_colsum", "fc_kv_importance_redundancy",
     "fc_kv_redundancy", "fc_kv_select", "fc_topb_select_workspace_bytes", "fc_topb_select",
     "fc_chunk_rel_l1_workspace_bytes", "fc_chunk_rel_l1_decide",
     "fc_cache_commit_workspace_bytes", "fc_cache_commit", "fc_euler_step_l1_decide",
@@ -68,6 +68,8 @@ _lib.fc_kv_compress.restype = ctypes.c_int
 _lib.fc_kv_compress.argtypes = [ctypes.POINTER(fc_kv_params)] + [_vp] * 9 + [_vp, _sz, _vp]
 _lib.fc_kv_importance.restype = ctypes.c_int
 _lib.fc_kv_importance.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.fc_kv_importance_redundancy.restype = ctypes.c_int
+_lib.fc_kv_importance_redundancy.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_importance_lse.restype = ctypes.c_int
 _lib.fc_kv_importance_lse.argtypes = [ctypes.POINTER(fc_kv_params), _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.fc_kv_importance_colsum.restype = ctypes.c_int
@@ -243,6 +245,24 @@ def fc_kv_importance(Q, K, softmax_scale: float = 0.0, imp_out=None, workspace=N
     _check("fc_kv_importance", _lib.fc_kv_importance(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(imp_out), _ptr(ws),
                                                      _nbytes(ws), _stream(stream)))
     return imp_out
+
+
+def fc_kv_importance_redundancy(Q, K, softmax_scale: float = 0.0, imp_out=None, r_out=None, workspace=None,
+                                stream=None):
+    """(importance before the pool, redundancy mean), both [H][L_k] f32, from
+    the launches of fc_kv_compress's first half."""
+    p = kv_params(Q, K, 1, 0.5, 1, softmax_scale)
+    H, Lk, _ = K.shape
+    if imp_out is None:
+        imp_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    if r_out is None:
+        r_out = torch.empty((H, Lk), dtype=torch.float32, device=K.device)
+    _expect("imp_out", imp_out, (H, Lk), torch.float32)
+    _expect("r_out", r_out, (H, Lk), torch.float32)
+    ws = _workspace(fc_kv_compress_workspace_bytes(p), K.device, workspace)
+    _check("fc_kv_importance_redundancy", _lib.fc_kv_importance_redundancy(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(imp_out), _ptr(r_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return imp_out, r_out
 
 
 def fc_kv_importance_lse(Q, K, softmax_scale: float = 0.0, lse_out=None, workspace=None, stream=None):

@@ -278,6 +278,18 @@ fc_status fc_kv_importance(const fc_kv_params* p, const void* Q, const void* K, 
     return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream));
 }
 
+fc_status fc_kv_importance_redundancy(const fc_kv_params* p, const void* Q, const void* K, float* imp_out,
+                                      float* r_out, void* workspace, size_t workspace_bytes, void* stream) {
+    fc_status st = check_kv(p);
+    if (st != FC_OK) return st;
+    if (!Q || !K || !imp_out || !r_out || !aligned16(Q) || !aligned16(K)) return FC_ERR_INVALID_ARG;
+    const KvLayout L = kv_layout(p);
+    if (!L.fits) return FC_ERR_UNSUPPORTED;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return FC_ERR_WORKSPACE;
+    // the launches of fc_kv_compress's first half, into the caller's arrays
+    return run_importance(p, L, Q, K, imp_out, workspace, static_cast<hipStream_t>(stream), r_out);
+}
+
 fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void* K, float* lse_out, void* workspace,
                                size_t workspace_bytes, void* stream) {
     fc_status st = check_kv(p);

@@ -115,31 +115,52 @@ def _apply_dup(cfg: KVConfig, x: np.ndarray) -> None:
     x[d0 * tpf:d1 * tpf] = x[s0 * tpf:s1 * tpf]
 
 
-def kv_inputs(cfg: KVConfig, seed: int = 0, heads: Optional[Sequence[int]] = None):
+def _kv_head(cfg: KVConfig, seed: int, h: int):
+    """Head h's (Q, K, V), float32, from its own streams."""
+    qs, kfs, kns, vs = _head_streams(seed, cfg.H)
+    Q = np.random.default_rng(qs[h]).standard_normal((cfg.Lq, cfg.d), dtype=np.float32)
+    V = np.random.default_rng(vs[h]).standard_normal((cfg.Lk, cfg.d), dtype=np.float32)
+    rf, rn = np.random.default_rng(kfs[h]), np.random.default_rng(kns[h])
+    if cfg.key_kind == "clustered":
+        base = rf.standard_normal((cfg.n_base, cfg.d), dtype=np.float32)
+        K = base[np.arange(cfg.Lk) // cfg.base_repeat] + \
+            cfg.base_noise * rn.standard_normal((cfg.Lk, cfg.d), dtype=np.float32)
+    elif cfg.key_kind == "field":
+        K = _field_keys(cfg, rf, rn)
+    else:
+        raise ValueError(cfg.key_kind)
+    _apply_dup(cfg, K)
+    _apply_dup(cfg, V)
+    return Q, K, V
+
+
+def kv_inputs(cfg: KVConfig, seed: int = 0, heads: Optional[Sequence[int]] = None, workers: int = 1):
     """(Q, K, V) as CPU tensors in the config's storage dtype, head-major
-    [H'][L][d], for the given heads (default: all)."""
+    [H'][L][d], for the given heads (default: all).  With workers > 1 the
+    heads are drawn on that many threads (the random draws and the filter
+    release the GIL); every head has its own streams, so the values do not
+    depend on the worker count."""
     if heads is None:
         heads = range(cfg.H)
     heads = list(heads)
-    qs, kfs, kns, vs = _head_streams(seed, cfg.H)
-    Q = np.empty((len(heads), cfg.Lq, cfg.d), np.float32)
-    K = np.empty((len(heads), cfg.Lk, cfg.d), np.float32)
-    V = np.empty((len(heads), cfg.Lk, cfg.d), np.float32)
-    for n, h in enumerate(heads):
-        Q[n] = np.random.default_rng(qs[h]).standard_normal((cfg.Lq, cfg.d), dtype=np.float32)
-        V[n] = np.random.default_rng(vs[h]).standard_normal((cfg.Lk, cfg.d), dtype=np.float32)
-        rf, rn = np.random.default_rng(kfs[h]), np.random.default_rng(kns[h])
-        if cfg.key_kind == "clustered":
-            base = rf.standard_normal((cfg.n_base, cfg.d), dtype=np.float32)
-            K[n] = base[np.arange(cfg.Lk) // cfg.base_repeat] + \
-                cfg.base_noise * rn.standard_normal((cfg.Lk, cfg.d), dtype=np.float32)
-        elif cfg.key_kind == "field":
-            K[n] = _field_keys(cfg, rf, rn)
-        else:
-            raise ValueError(cfg.key_kind)
-        _apply_dup(cfg, K[n])
-        _apply_dup(cfg, V[n])
-    return _to_storage(Q, cfg.dtype), _to_storage(K, cfg.dtype), _to_storage(V, cfg.dtype)
+    n_h = len(heads)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    Q = torch.empty((n_h, cfg.Lq, cfg.d), dtype=dt)
+    K = torch.empty((n_h, cfg.Lk, cfg.d), dtype=dt)
+    V = torch.empty((n_h, cfg.Lk, cfg.d), dtype=dt)
+
+    def one(n):
+        for dst, x in zip((Q, K, V), _kv_head(cfg, seed, heads[n])):
+            dst[n] = _to_storage(x, cfg.dtype)
+
+    if workers > 1 and n_h > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(workers, n_h)) as ex:
+            list(ex.map(one, range(n_h)))
+    else:
+        for n in range(n_h):
+            one(n)
+    return Q, K, V
 
 
 def random_kv(H: int, Lq: int, Lk: int, d: int, dtype: str, seed: int):

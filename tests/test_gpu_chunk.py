@@ -23,17 +23,32 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_trajectory(fc, cfg, eps_list, g_steps=None, seed=0):
+def oracle_l1_rel(xt, xtm1, offsets, threads=8):
+    """The oracle's L1_rel of every chunk; chunks on separate threads (the
+    fp64 sums of one chunk stay whole, in one call of the oracle)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(i):
+        s, e = offsets[i], offsets[i + 1]
+        return oracle.chunk_l1_rel(xt[s:e], xtm1[s:e], [0, e - s])[0]
+    with ThreadPoolExecutor(threads) as ex:
+        return np.array(list(ex.map(one, range(len(offsets) - 1))))
+
+
+def run_trajectory(fc, cfg, eps_list, g_steps=None, seed=0, m_list=None):
+    """Deciders for every (m, eps) in zip(m_list, eps_list) (m_list defaults
+    to cfg.m for all) in lockstep with the oracle over the trajectory."""
     tr = synth.ChunkTrajectory(cfg, seed=seed)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    decs = [fc.ChunkDecider(tr.offsets, cfg.m, e, dt, DEV) for e in eps_list]
-    locks = [Lockstep(cfg.n_chunks, cfg.m, e) for e in eps_list]
+    m_list = [cfg.m] * len(eps_list) if m_list is None else m_list
+    decs = [fc.ChunkDecider(tr.offsets, m, e, dt, DEV) for m, e in zip(m_list, eps_list)]
+    locks = [Lockstep(cfg.n_chunks, m, e) for m, e in zip(m_list, eps_list)]
     g_steps = range(tr.n_global_steps()) if g_steps is None else g_steps
     for g in g_steps:
         xt, xtm1, steps = tr.pair(g)
         st = torch.tensor(steps, dtype=torch.int32)
         xt_d, xtm1_d = xt.to(DEV), xtm1.to(DEV)
-        l1_ref = oracle.chunk_l1_rel(xt, xtm1, tr.offsets)
+        l1_ref = oracle_l1_rel(xt, xtm1, tr.offsets)
         for dec, lk in zip(decs, locks):
             # chunks that start now enter at local step 0; finished ones leave (-1)
             cur = dec.step.cpu()
@@ -61,13 +76,21 @@ def test_tiny_trajectory_other_thresholds(fc, seed):
     assert all(lk.decisions == cfg.n_chunks * cfg.N for lk in locks)
 
 
-def test_scale_trajectory_first_steps(fc):
-    # 16 chunks x 7,372,800 bf16, staggered starts; the first 24 global steps
-    # cover every chunk's forced steps and many threshold decisions
+@pytest.mark.timeout(600)
+def test_scale_trajectory_full(fc):
+    # 16 chunks x 7,372,800 bf16, staggered starts: every one of the 65 global
+    # steps (each chunk's 50 local steps, the reuse-heavy small-step end of
+    # the schedule included) with MAGI-1's settings (m = 5, eps 0.01 and
+    # 0.015) and SkyReels-V2's (m = 4, eps 0.1 and 0.15), four deciders in
+    # lockstep with the oracle on the same states
     cfg = synth.CHUNK_CONFIGS["scale"]
-    say("case: 16 chunks x 64x8x90x160 bf16, global steps 0..23, eps 0.01 and 0.015")
-    locks = run_trajectory(fc, cfg, cfg.eps, g_steps=range(24))
-    assert all(lk.decisions > 100 for lk in locks)
+    m_list, eps_list = [5, 5, 4, 4], [0.01, 0.015, 0.1, 0.15]
+    say("case: 16 chunks x 64x8x90x160 bf16, all 65 global steps, (m, eps) = "
+        + ", ".join(f"({m}, {e})" for m, e in zip(m_list, eps_list)))
+    locks = run_trajectory(fc, cfg, eps_list, m_list=m_list)
+    for lk, m, e in zip(locks, m_list, eps_list):
+        assert lk.decisions == cfg.n_chunks * cfg.N
+        say(f"  m={m} eps={e}: {lk.decisions} decisions, {lk.exempt} inside the 1e-6 band")
 
 
 def test_unaligned_offsets_and_edge_chunks(fc):

@@ -253,3 +253,29 @@ def test_importance_wide_logit_range(fc, dtype, d):
     assert float(np.max(np.abs(got[big] - want[big]) / want[big])) <= parity.REL or \
         float(np.max(np.abs(got - want))) <= 1e-6
     np.testing.assert_allclose(lse.cpu().double().numpy(), oracle.lse(Qt, Kt, 1.0), rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk", [("bf16", 128, 3, 300, 5000), ("f32", 64, 2, 70, 777),
+                                             ("bf16", 64, 2, 2500, 500)])
+def test_importance_redundancy_stage(fc, dtype, d, H, Lq, Lk):
+    """The compression's first half as a stage: the importance bit-identical to
+    fc_kv_importance's, the redundancy against the oracle (as the stand-alone
+    stage is), and both fed to fc_kv_select give fc_kv_compress's result."""
+    Q, K, V = synth.random_kv(H, Lq, Lk, d, dtype, seed=21)
+    say(f"case: fc_kv_importance_redundancy {dtype} d={d} H={H} Lq={Lq} Lk={Lk}")
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    imp, r = fc.fc_kv_importance_redundancy(Qd, Kd)
+    imp_alone = fc.fc_kv_importance(Qd, Kd)
+    torch.cuda.synchronize()
+    assert torch.equal(imp.view(torch.int32), imp_alone.view(torch.int32))
+    want_imp = oracle.importance(Q, K, 1 / math.sqrt(d))
+    assert parity.max_rel_err(imp.cpu().numpy(), want_imp) <= parity.REL
+    want_r = oracle.redundancy_mean(K)
+    assert float(np.max(np.abs(r.cpu().double().numpy() - want_r))) <= 1e-5
+    B = Lk // 3
+    sel = fc.fc_kv_select(imp, r, B, 0.5, 7, Kd, Vd, want_scores=False)
+    full = fc.fc_kv_compress(Qd, Kd, Vd, B, 0.5, 7)
+    torch.cuda.synchronize()
+    ref = oracle.kv_compress(Q, K, V, B, 0.5, 7)
+    parity.check_selection(sel["idx"], ref["score"], B)
+    parity.check_selection(full["idx"], ref["score"], B)
