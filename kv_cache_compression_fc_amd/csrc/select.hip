@@ -423,48 +423,86 @@ __global__ __launch_bounds__(kSelThreads) void sel_head_kernel(
 }
 
 // ---- selection split over several workgroups per head ----------------------------------
-// For heads longer than one workgroup's share, the same exact selection runs
-// as four launches of G workgroups per head, each workgroup owning S
+// For heads longer than one chunk the same exact selection runs as five
+// launches of G workgroups per head, each workgroup owning S <= 4096
 // consecutive keys [g S, g S + S):
 //   keys:    pool + score + order-preserving key of its keys, written to the
-//            workspace, and the workgroup's histogram of the top 8 key bits;
-//            it also clears the head's round-1 and round-2 histograms;
-//   round 1: the head's round-0 histogram (sum of the G partial ones) gives
-//            the bin b0 of the B'-th largest key; the workgroup counts bits
-//            23..12 of its keys in bin b0 and adds its nonzero bins into the
-//            head's histogram with integer atomics (the counts, and so every
-//            later step, do not depend on their order);
-//   round 2: likewise for bits 11..0 of the keys whose top 20 bits are the
-//            prefix found so far; the workgroup also writes how many of its
-//            keys lie above that prefix and its counts per low-12-bit bin as
-//            suffix sums, so the compaction can count the keys of earlier
-//            workgroups above and at the threshold with two reads each;
+//            workspace, and the workgroup's 256-bin histogram of key bits
+//            31..24;
+//   round R (R = 1, 2, 3): the head's histogram of the previous round (the
+//            sum of the G partial ones, in workgroup order) gives the bin of
+//            the B'-th largest key among those matching the prefix found so
+//            far, so the prefix grows by 8 bits; the workgroup writes its
+//            256-bin histogram of the next 8 bits of its keys that match it.
+//            Round 3 also writes, per workgroup, how many of its keys lie
+//            above the 24-bit prefix and its suffix counts per low-8-bit bin,
+//            so the compaction counts the keys of earlier workgroups above
+//            and at the threshold with two reads each;
 //   compact: the threshold key T and the number q of keys equal to T that
-//            fit come from the head's round-2 histogram; the workgroup's
+//            fit come from the head's round-3 histogram; the workgroup's
 //            output offset is the kept keys of the earlier workgroups, and its
 //            kept indices (every key > T, the equal keys while fewer than q
 //            lie before them in token order) go out ascending.
-// Separate launches order the phases: no grid barrier, no spin-wait.
+// Integer counts only, no atomics outside LDS: deterministic.  Separate
+// launches order the phases (no grid barrier, no spin-wait); every small
+// global read of a phase is issued before any is waited for.
 constexpr int kMT = 512;                  // threads per workgroup
 constexpr int kMWaves = kMT / kWave;
-constexpr int kMKpt = 16;                 // consecutive keys per thread
-constexpr int kMMaxKeys = kMT * kMKpt;    // 8192: most keys one workgroup owns
-constexpr int kRBins = 4096;              // bins of rounds 1 and 2
-constexpr int kRCopies = 4;               // LDS copies of each round-1/2 bin
-constexpr int kR0Copies = 8;              // LDS copies of each round-0 bin
-constexpr int kCum = kRBins + 4;          // per-workgroup suffix counts (4097 used)
+constexpr int kMKpt = 8;                  // consecutive keys per thread
+constexpr int kMMaxKeys = kMT * kMKpt;    // 4096: most keys one workgroup owns
+constexpr int kR0Copies = 16;             // LDS copies of each round-0 bin (scores share their top bits)
+constexpr int kRCopies = 4;               // LDS copies of each later bin
+constexpr int kCum = 260;                 // per-workgroup suffix counts (257 used)
 static_assert(kMMaxKeys < 65536, "packed 16-bit counts of one workgroup");
 
 // Workspace of the split selection, per head h and workgroup g.
 struct MselWs {
-    uint32_t* keys;   // [H][L] order-preserving keys
-    uint32_t* hist0;  // [H][G][256] round-0 counts per workgroup
-    uint32_t* h1;     // [H][4096] round-1 counts of the head
-    uint32_t* h2;     // [H][4096] round-2 counts of the head
-    uint32_t* gt20;   // [H][G] keys above the 20-bit prefix per workgroup
-    uint32_t* cum2;   // [H][G][kCum] suffix counts of the prefix-matching keys per low-12-bit bin
-    uint32_t* state;  // [H][4] b0, k1, b1, k2
+    uint32_t* keys;     // [H][L] order-preserving keys
+    uint32_t* hist[4];  // [H][G][256] per-workgroup histograms of rounds 0..3
+    uint32_t* above;    // [H][G] keys above the 24-bit prefix per workgroup
+    uint32_t* cum3;     // [H][G][kCum] suffix counts of the prefix-matching keys per low-8-bit bin
+    uint32_t* state;    // [H][4][2] (prefix, rank in its bin) after rounds 1..3
 };
+
+// Work item of a split-selection workgroup: (head, workgroup of the head).
+__device__ __forceinline__ bool msel_item(int H, int G, int& h, int& g) {
+    const int item = xcd_item((int)(gridDim.x / 8u));
+    if (item >= H * G) return false;
+    h = item / G;
+    g = item % G;
+    return true;
+}
+
+// tot[256] = the head's histogram of a round: the sum of its G per-workgroup
+// rows, in workgroup order per bin.  Thread t adds 4 bins (column t % 64) of
+// the rows w = t/64, t/64 + 8, ... (loads issued four at a time), then the
+// eight partial sums per bin are added.
+__device__ __forceinline__ void msel_sum_rows(const uint32_t* __restrict__ rows, int G, uint32_t* part,
+                                              uint32_t* tot) {
+    const int tid = threadIdx.x, col = tid & 63, w0 = tid >> 6;
+    const uint4* r4 = reinterpret_cast<const uint4*>(rows);
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    int w = w0;
+    for (; w + 24 < G; w += 32) {
+        const uint4 a = r4[(size_t)w * 64 + col], b = r4[(size_t)(w + 8) * 64 + col];
+        const uint4 c = r4[(size_t)(w + 16) * 64 + col], d = r4[(size_t)(w + 24) * 64 + col];
+        acc.x += a.x + b.x + c.x + d.x; acc.y += a.y + b.y + c.y + d.y;
+        acc.z += a.z + b.z + c.z + d.z; acc.w += a.w + b.w + c.w + d.w;
+    }
+    for (; w < G; w += 8) {
+        const uint4 a = r4[(size_t)w * 64 + col];
+        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+    }
+    reinterpret_cast<uint4*>(part)[w0 * 64 + col] = acc;
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c += part[k * 256 + tid];
+        tot[tid] = c;
+    }
+    __syncthreads();
+}
 
 template <bool kFromImp>
 __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict__ src, int nsrc,
@@ -479,56 +517,83 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
     __shared__ __align__(16) float it[kMMaxKeys + 2 * kMaxHalo];
     __shared__ __align__(16) uint32_t kt[kMMaxKeys];
     __shared__ uint32_t hist[256 * kR0Copies];
-    __shared__ float stat[2];
-    const int n_items = H * G;
-    const int item = xcd_item((int)(gridDim.x / 8u));
-    if (item >= n_items) return;
-    const int h = item / G, g = item % G, tid = threadIdx.x;
+    __shared__ float2 wstat[kMWaves];
+    int h, g;
+    if (!msel_item(H, G, h, g)) return;
+    const int tid = threadIdx.x;
     const int j0 = g * S, n = min(S, L - j0);
     const size_t hL = (size_t)h * L;
     const size_t plane = (size_t)H * L;
 
-    for (int b = tid; b < 256 * kR0Copies; b += kMT) hist[b] = 0u;
+    // every global read of the phase first: r (or the scores), the
+    // importance with its halo, the redundancy softmax partials
     const float* rs = (kFromImp ? r : src) + hL + j0;
+    float vr[kMKpt];
 #pragma unroll
     for (int q = 0; q < kMKpt; ++q) {
         const int i = tid + q * kMT;
-        if (i < n) kt[i] = __float_as_uint(rs[i]);
+        vr[q] = i < n ? rs[i] : 0.f;
+    }
+    constexpr int kQa = (kMMaxKeys + 2 * kMaxHalo + kMT - 1) / kMT;
+    float vi[kQa];
+    float M = -1e30f, Sm = 0.f;
+    if constexpr (kFromImp) {
+#pragma unroll
+        for (int q = 0; q < kQa; ++q) {
+            const int i = tid + q * kMT, j = j0 - kMaxHalo + i;
+            vi[q] = (i < n + 2 * kMaxHalo && j >= 0 && j < L) ? src[hL + j] : -INFINITY;
+        }
+        for (int pl = 1; pl < nsrc; ++pl) {
+#pragma unroll
+            for (int q = 0; q < kQa; ++q) {
+                const int i = tid + q * kMT, j = j0 - kMaxHalo + i;
+                if (i < n + 2 * kMaxHalo && j >= 0 && j < L) vi[q] += src[pl * plane + hL + j];
+            }
+        }
+        // softmax statistics of r: (max of r log2 e, sum 2^{r log2 e - max}) over
+        // the head's partials, four loads in flight per thread
+        const float2* rp = red_part + (size_t)h * nbr;
+        int i = tid;
+        for (; i + 3 * kMT < nbr; i += 4 * kMT) {
+            const float2 a = rp[i], b = rp[i + kMT], c = rp[i + 2 * kMT], d = rp[i + 3 * kMT];
+            lse2_merge(M, Sm, a.x, a.y);
+            lse2_merge(M, Sm, b.x, b.y);
+            lse2_merge(M, Sm, c.x, c.y);
+            lse2_merge(M, Sm, d.x, d.y);
+        }
+        for (; i < nbr; i += kMT) {
+            const float2 a = rp[i];
+            lse2_merge(M, Sm, a.x, a.y);
+        }
+    }
+    for (int b = tid; b < 256 * kR0Copies; b += kMT) hist[b] = 0u;
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        if (i < n) kt[i] = __float_as_uint(vr[q]);
     }
     if constexpr (kFromImp) {
-        constexpr int kQa = (kMMaxKeys + 2 * kMaxHalo + kMT - 1) / kMT;
 #pragma unroll
         for (int q = 0; q < kQa; ++q) {
             const int i = tid + q * kMT;
-            if (i < n + 2 * kMaxHalo) {
-                const int j = j0 - kMaxHalo + i;
-                float v = -INFINITY;
-                if (j >= 0 && j < L) {
-                    v = src[hL + j];
-                    for (int pl = 1; pl < nsrc; ++pl) v += src[pl * plane + hL + j];
-                }
-                it[i] = v;
-            }
+            if (i < n + 2 * kMaxHalo) it[i] = vi[q];
         }
-        // softmax statistics of r: (max of r log2 e, 1 / sum 2^{r log2 e - max})
-        if (tid < kWave) {
-            float M = -1e30f, Sm = 0.f;
-            for (int i = tid; i < nbr; i += kWave) {
-                const float2 v = red_part[(size_t)h * nbr + i];
-                lse2_merge(M, Sm, v.x, v.y);
-            }
 #pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(Sm, o, kWave);
-                lse2_merge(M, Sm, m2, s2);
-            }
-            if (tid == 0) {
-                stat[0] = M;
-                stat[1] = 1.0f / Sm;
-            }
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(Sm, o, kWave);
+            lse2_merge(M, Sm, m2, s2);
         }
+        if ((tid & (kWave - 1)) == 0) wstat[tid / kWave] = make_float2(M, Sm);
     }
     __syncthreads();
+    float invS = 0.f;
+    if constexpr (kFromImp) {
+        M = wstat[0].x;
+        Sm = wstat[0].y;
+#pragma unroll
+        for (int w = 1; w < kMWaves; ++w) lse2_merge(M, Sm, wstat[w].x, wstat[w].y);
+        invS = 1.0f / Sm;
+    }
 
     const int x0 = tid * kMKpt;
     const uint32_t copy = tid & (kR0Copies - 1);
@@ -556,7 +621,6 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
             }
         }
     }
-    const float M = kFromImp ? stat[0] : 0.f, invS = kFromImp ? stat[1] : 0.f;
 #pragma unroll
     for (int i = 0; i < kMKpt; ++i) {
         const int x = x0 + i;
@@ -587,158 +651,122 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
         uint32_t c = 0;
 #pragma unroll
         for (int cp = 0; cp < kR0Copies; ++cp) c += hist[tid * kR0Copies + cp];
-        ws.hist0[((size_t)h * G + g) * 256 + tid] = c;
-    }
-    // the head's round-1 and round-2 histograms start at zero
-    for (int b = g * kMT + tid; b < kRBins; b += G * kMT) {
-        ws.h1[(size_t)h * kRBins + b] = 0u;
-        ws.h2[(size_t)h * kRBins + b] = 0u;
+        ws.hist[0][((size_t)h * G + g) * 256 + tid] = c;
     }
 }
 
-__global__ __launch_bounds__(kMT) void msel_round1_kernel(int H, int L, int G, int S, int Bp, MselWs ws) {
-    __shared__ uint32_t hist[kRBins * kRCopies];
-    __shared__ uint32_t tot0[256];
+// Round R = 1, 2, 3: the bin of the previous round's head histogram that
+// holds the B'-th largest key extends the prefix by 8 bits; the workgroup's
+// histogram of the next 8 bits of its keys that match the new prefix.
+template <int R>
+__global__ __launch_bounds__(kMT) void msel_round_kernel(int H, int L, int G, int S, int Bp, MselWs ws) {
+    constexpr int kShift = 24 - 8 * R;   // the bits this round counts: (key >> kShift) & 0xff
+    __shared__ uint32_t hist[256 * kRCopies];
+    __shared__ __align__(16) uint32_t part[8 * 256];
+    __shared__ uint32_t tot[256];
     __shared__ uint32_t scan_lds[kMWaves];
     __shared__ uint32_t s_res[2];
-    const int item = xcd_item((int)(gridDim.x / 8u));
-    if (item >= H * G) return;
-    const int h = item / G, g = item % G, tid = threadIdx.x;
+    int h, g;
+    if (!msel_item(H, G, h, g)) return;
+    const int tid = threadIdx.x;
     const int j0 = g * S, n = min(S, L - j0);
-    if (tid < 256) {
-        uint32_t c = 0;
-        for (int w = 0; w < G; ++w) c += ws.hist0[((size_t)h * G + w) * 256 + tid];
-        tot0[tid] = c;
+    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
+    uint32_t kv[kMKpt];
+#pragma unroll
+    for (int q = 0; q < kMKpt; ++q) {
+        const int i = tid + q * kMT;
+        kv[q] = i < n ? kg[i] : 0u;
     }
-    for (int b = tid; b < kRBins * kRCopies; b += kMT) hist[b] = 0u;
-    __syncthreads();
+    // prefix and rank so far (round 1: none, rank B')
+    const uint32_t P0 = R == 1 ? 0u : ws.state[(h * 4 + R - 1) * 2 + 0];
+    const uint32_t k0 = R == 1 ? (uint32_t)Bp : ws.state[(h * 4 + R - 1) * 2 + 1];
+    for (int b = tid; b < 256 * kRCopies; b += kMT) hist[b] = 0u;
+    msel_sum_rows(ws.hist[R - 1] + (size_t)h * G * 256, G, part, tot);
     uint32_t k1;
-    const uint32_t b0 = find_bin_from_top<256, 1, kMT>(tot0, (uint32_t)Bp, &k1, scan_lds, s_res);
-    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
-    const uint32_t copy = tid & (kRCopies - 1);
-    uint32_t kv[kMKpt];
-#pragma unroll
-    for (int q = 0; q < kMKpt; ++q) {
-        const int i = tid + q * kMT;
-        kv[q] = i < n ? kg[i] : 0u;
-    }
-#pragma unroll
-    for (int q = 0; q < kMKpt; ++q) {
-        const int i = tid + q * kMT;
-        if (i < n && (kv[q] >> 24) == b0) atomicAdd(&hist[((kv[q] >> 12) & (kRBins - 1)) * kRCopies + copy], 1u);
-    }
-    __syncthreads();
-    for (int b = tid; b < kRBins; b += kMT) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int cp = 0; cp < kRCopies; ++cp) c += hist[b * kRCopies + cp];
-        if (c) atomicAdd(&ws.h1[(size_t)h * kRBins + b], c);
-    }
-    if (g == 0 && tid == 0) {
-        ws.state[h * 4 + 0] = b0;
-        ws.state[h * 4 + 1] = k1;
-    }
-}
-
-__global__ __launch_bounds__(kMT) void msel_round2_kernel(int H, int L, int G, int S, MselWs ws) {
-    __shared__ uint32_t hist[kRBins * kRCopies];
-    __shared__ uint32_t scan_lds[kMWaves];
-    __shared__ uint32_t s_res[2];
-    const int item = xcd_item((int)(gridDim.x / 8u));
-    if (item >= H * G) return;
-    const int h = item / G, g = item % G, tid = threadIdx.x;
-    const int j0 = g * S, n = min(S, L - j0);
-    const uint32_t b0 = ws.state[h * 4 + 0], k1 = ws.state[h * 4 + 1];
-    for (int b = tid; b < kRBins; b += kMT) hist[b] = ws.h1[(size_t)h * kRBins + b];
-    const uint32_t* kg = ws.keys + (size_t)h * L + j0;
-    uint32_t kv[kMKpt];
-#pragma unroll
-    for (int q = 0; q < kMKpt; ++q) {
-        const int i = tid + q * kMT;
-        kv[q] = i < n ? kg[i] : 0u;
-    }
-    __syncthreads();
-    uint32_t k2;
-    const uint32_t b1 = find_bin_from_top<kRBins, 1, kMT>(hist, k1, &k2, scan_lds, s_res);
-    const uint32_t pre2 = (b0 << 12) | b1;  // top 20 bits of the threshold
-    for (int b = tid; b < kRBins * kRCopies; b += kMT) hist[b] = 0u;
-    __syncthreads();
+    const uint32_t bin = find_bin_from_top<256, 1, kMT>(tot, k0, &k1, scan_lds, s_res);
+    const uint32_t P = (P0 << 8) | bin;  // the top 8 R bits of the threshold
     const uint32_t copy = tid & (kRCopies - 1);
     uint32_t above = 0;
 #pragma unroll
     for (int q = 0; q < kMKpt; ++q) {
         const int i = tid + q * kMT;
         if (i < n) {
-            const uint32_t p = kv[q] >> 12;
-            if (p == pre2) atomicAdd(&hist[(kv[q] & (kRBins - 1)) * kRCopies + copy], 1u);
-            above += p > pre2;
+            const uint32_t p = kv[q] >> (kShift + 8);
+            if (p == P) atomicAdd(&hist[((kv[q] >> kShift) & 0xffu) * kRCopies + copy], 1u);
+            if (R == 3) above += p > P;
         }
     }
     __syncthreads();
-    // thread t owns bins 4095 - (8t + i), i = 0..7 (descending): suffix counts
-    constexpr int kPer = kRBins / kMT;
-    uint32_t cnt[kPer], mine = 0;
+    if constexpr (R < 3) {
+        if (tid < 256) {
+            uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int b = kRBins - 1 - (tid * kPer + i);
+            for (int cp = 0; cp < kRCopies; ++cp) c += hist[tid * kRCopies + cp];
+            ws.hist[R][((size_t)h * G + g) * 256 + tid] = c;
+        }
+    } else {
+        // thread t < 256 owns bin 255 - t: suffix counts by a scan in
+        // descending bin order
         uint32_t c = 0;
+        if (tid < 256) {
 #pragma unroll
-        for (int cp = 0; cp < kRCopies; ++cp) c += hist[b * kRCopies + cp];
-        cnt[i] = c;
-        mine += c;
+            for (int cp = 0; cp < kRCopies; ++cp) c += hist[(255 - tid) * kRCopies + cp];
+            ws.hist[3][((size_t)h * G + g) * 256 + 255 - tid] = c;
+        }
+        uint32_t t1;
+        const uint32_t before = block_exclusive_scan<kMT>(c, scan_lds, &t1);
+        uint32_t* cum = ws.cum3 + ((size_t)h * G + g) * kCum;
+        if (tid < 256) cum[255 - tid] = before + c;  // prefix-matching keys with low 8 bits >= the bin
+        if (tid == 0) cum[256] = 0u;
+        uint32_t t2;
+        (void)block_exclusive_scan<kMT>(above, scan_lds, &t2);
+        if (tid == 0) ws.above[(size_t)h * G + g] = t2;
     }
-    uint32_t tot;
-    uint32_t run = block_exclusive_scan<kMT>(mine, scan_lds, &tot);
-    uint32_t* cum = ws.cum2 + ((size_t)h * G + g) * kCum;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int b = kRBins - 1 - (tid * kPer + i);
-        run += cnt[i];
-        cum[b] = run;  // keys matching the prefix with low 12 bits >= b
-        if (cnt[i]) atomicAdd(&ws.h2[(size_t)h * kRBins + b], cnt[i]);
-    }
-    if (tid == 0) cum[kRBins] = 0u;
-    const uint32_t above_all = block_exclusive_scan<kMT>(above, scan_lds, &tot);
-    (void)above_all;
-    if (tid == 0) ws.gt20[(size_t)h * G + g] = tot;
     if (g == 0 && tid == 0) {
-        ws.state[h * 4 + 2] = b1;
-        ws.state[h * 4 + 3] = k2;
+        ws.state[(h * 4 + R) * 2 + 0] = P;
+        ws.state[(h * 4 + R) * 2 + 1] = k1;
     }
 }
 
 __global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, int S, int Bp, MselWs ws,
                                                            int32_t* __restrict__ idx_out) {
-    __shared__ uint32_t hist[kRBins];
+    __shared__ __align__(16) uint32_t part[8 * 256];
+    __shared__ uint32_t tot[256];
     __shared__ __align__(16) uint32_t kt[kMMaxKeys];
     __shared__ uint32_t scan_lds[kMWaves];
     __shared__ uint32_t s_res[2];
-    const int item = xcd_item((int)(gridDim.x / 8u));
-    if (item >= H * G) return;
-    const int h = item / G, g = item % G, tid = threadIdx.x;
+    int h, g;
+    if (!msel_item(H, G, h, g)) return;
+    const int tid = threadIdx.x;
     const int j0 = g * S, n = min(S, L - j0);
-    const uint32_t b0 = ws.state[h * 4 + 0], b1 = ws.state[h * 4 + 2], k2 = ws.state[h * 4 + 3];
-    for (int b = tid; b < kRBins; b += kMT) hist[b] = ws.h2[(size_t)h * kRBins + b];
     const uint32_t* kg = ws.keys + (size_t)h * L + j0;
+    uint32_t kq[kMKpt];
 #pragma unroll
     for (int q = 0; q < kMKpt; ++q) {
         const int i = tid + q * kMT;
-        if (i < n) kt[i] = kg[i];
+        kq[q] = i < n ? kg[i] : 0u;
     }
-    __syncthreads();
+    const uint32_t P3 = ws.state[(h * 4 + 3) * 2 + 0], k3 = ws.state[(h * 4 + 3) * 2 + 1];
+    // keys above the 24-bit prefix and suffix counts of the earlier workgroups
+    // (read before the bin is known: both candidate entries come later)
+    msel_sum_rows(ws.hist[3] + (size_t)h * G * 256, G, part, tot);
     uint32_t q;
-    const uint32_t b2 = find_bin_from_top<kRBins, 1, kMT>(hist, k2, &q, scan_lds, s_res);
-    const uint32_t T = (b0 << 24) | (b1 << 12) | b2;  // the B'-th largest key; q of the keys equal to T fit
-    // keys above T and equal to T in the earlier workgroups of the head
+    const uint32_t b3 = find_bin_from_top<256, 1, kMT>(tot, k3, &q, scan_lds, s_res);
+    const uint32_t T = (P3 << 8) | b3;  // the B'-th largest key; q of the keys equal to T fit
     uint32_t gt_p = 0, eq_p = 0;
     for (int w = tid; w < g; w += kMT) {
-        const uint32_t* cum = ws.cum2 + ((size_t)h * G + w) * kCum;
-        const uint32_t hi = cum[b2 + 1];
-        gt_p += ws.gt20[(size_t)h * G + w] + hi;
-        eq_p += cum[b2] - hi;
+        const uint32_t* cum = ws.cum3 + ((size_t)h * G + w) * kCum;
+        const uint32_t hi = cum[b3 + 1];
+        gt_p += ws.above[(size_t)h * G + w] + hi;
+        eq_p += cum[b3] - hi;
+    }
+#pragma unroll
+    for (int qq = 0; qq < kMKpt; ++qq) {
+        const int i = tid + qq * kMT;
+        if (i < n) kt[i] = kq[qq];
     }
     uint32_t gt_before, eq_before;
-    (void)block_exclusive_scan<kMT>(gt_p, scan_lds, &gt_before);
+    (void)block_exclusive_scan<kMT>(gt_p, scan_lds, &gt_before);  // (its barriers also publish kt)
     (void)block_exclusive_scan<kMT>(eq_p, scan_lds, &eq_before);
     // this thread's consecutive keys, in token order
     const int x0 = tid * kMKpt;
@@ -750,10 +778,10 @@ __global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, 
         ngt += (x0 + i < n && kv[i] > T);
         neq += (x0 + i < n && kv[i] == T);
     }
-    uint32_t tot;
-    const uint32_t before = block_exclusive_scan<kMT>(ngt | (neq << 16), scan_lds, &tot);  // also orders kt's reuse
+    uint32_t totc;
+    const uint32_t before = block_exclusive_scan<kMT>(ngt | (neq << 16), scan_lds, &totc);  // also orders kt's reuse
     const uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
-    const uint32_t tot_gt = tot & 0xffffu, tot_eq = tot >> 16;
+    const uint32_t tot_gt = totc & 0xffffu, tot_eq = totc >> 16;
     const uint32_t eq_kept_b = min(eq_before + eq_b, q) - min(eq_before, q);
     const uint32_t tot_sel = tot_gt + min(eq_before + tot_eq, q) - min(eq_before, q);
     uint32_t eq_rank = eq_before + eq_b;
@@ -847,13 +875,14 @@ struct MselPlan {
 };
 
 // Heads of one chunk keep the one-workgroup kernel (its keys stay in LDS
-// between the passes).  Longer heads split into G workgroups of S <= 8192
+// between the passes).  Longer heads split into G workgroups of S <= 4096
 // consecutive keys: at least 1024 keys each, and enough workgroups for about
-// two per compute unit of a 256-CU device when the heads are few.
+// three per compute unit of a 256-CU device (one round of the grid) when the
+// heads are few.
 MselPlan msel_plan(int H, int L) {
     if (L <= kChunk) return MselPlan{0, 0};
     long long G = (L + kMMaxKeys - 1) / kMMaxKeys;
-    const long long g_fill = (512 + H - 1) / H, g_max = (L + 1023) / 1024;
+    const long long g_fill = 768 / H, g_max = (L + 1023) / 1024;
     const long long g_want = g_fill < g_max ? g_fill : g_max;
     if (g_want > G) G = g_want;
     const int S = (int)((L + G - 1) / G);
@@ -863,39 +892,39 @@ MselPlan msel_plan(int H, int L) {
 constexpr size_t kWsAlign = 256;
 size_t ws_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-// Layout of the selection workspace: keys, then (split plans only) the
-// histograms, counts and per-head state.  Offsets in bytes; [7] = total.
-void msel_offsets(int H, int L, const MselPlan& mp, size_t (&o)[8]) {
+// Layout of the selection workspace: keys, then (split plans only) the four
+// histogram arrays, the counts and the per-head state.  Offsets in bytes;
+// [9] = total.
+void msel_offsets(int H, int L, const MselPlan& mp, size_t (&o)[10]) {
     const size_t h = (size_t)H, G = (size_t)mp.G;
     size_t x = 0;
     o[0] = x; x = ws_up(x + h * (size_t)L * 4);  // keys
     if (mp.G > 0) {
-        o[1] = x; x = ws_up(x + h * G * 256 * 4);
-        o[2] = x; x = ws_up(x + h * kRBins * 4);
-        o[3] = x; x = ws_up(x + h * kRBins * 4);
-        o[4] = x; x = ws_up(x + h * G * 4);
-        o[5] = x; x = ws_up(x + h * G * kCum * 4);
-        o[6] = x; x = ws_up(x + h * 4 * 4);
+        for (int r = 0; r < 4; ++r) { o[1 + r] = x; x = ws_up(x + h * G * 256 * 4); }
+        o[5] = x; x = ws_up(x + h * G * 4);
+        o[6] = x; x = ws_up(x + h * G * kCum * 4);
+        o[7] = x; x = ws_up(x + h * 4 * 2 * 4);
     } else {
-        for (int i = 1; i < 7; ++i) o[i] = x;
+        for (int i = 1; i < 8; ++i) o[i] = x;
     }
-    o[7] = x;
+    o[8] = x;
+    o[9] = x;
 }
 
 MselWs msel_carve(void* base, int H, int L, const MselPlan& mp) {
-    size_t o[8];
+    size_t o[10];
     msel_offsets(H, L, mp, o);
     auto at = [&](int i) { return reinterpret_cast<uint32_t*>(static_cast<char*>(base) + o[i]); };
-    return MselWs{at(0), at(1), at(2), at(3), at(4), at(5), at(6)};
+    return MselWs{at(0), {at(1), at(2), at(3), at(4)}, at(5), at(6), at(7)};
 }
 
 }  // namespace
 
 size_t sel_ws_bytes(int H, int L) {
     const MselPlan mp = msel_plan(H, L);
-    size_t o[8];
+    size_t o[10];
     msel_offsets(H, L, mp, o);
-    return o[7];
+    return o[9];
 }
 
 bool sel_grid_fits(int H, int L) {
@@ -922,8 +951,9 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
         else
             hipLaunchKernelGGL(msel_keys_kernel<false>, grid, dim3(kMT), 0, s, src, 1, nullptr, nullptr, 0, 0.f, 0,
                                nullptr, nullptr, nullptr, H, L, mp.G, mp.S, ws);
-        hipLaunchKernelGGL(msel_round1_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws);
-        hipLaunchKernelGGL(msel_round2_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, ws);
+        hipLaunchKernelGGL(msel_round_kernel<1>, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws);
+        hipLaunchKernelGGL(msel_round_kernel<2>, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws);
+        hipLaunchKernelGGL(msel_round_kernel<3>, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws);
         hipLaunchKernelGGL(msel_compact_kernel, grid, dim3(kMT), 0, s, H, L, mp.G, mp.S, Bp, ws, idx_out);
         return hipGetLastError();
     }
