@@ -30,7 +30,7 @@ struct KvLayout {
     int nbu, nbr;
     int nkb;  // importance pass-2 workgroups per head (redundancy softmax partials of the fused path)
     bool fits;  // every launch of the plan fits a dispatch
-    size_t part, nlse2, imp, r, u_part, u, red_part, keys, total;
+    size_t part, nlse2, imp, r, u_part, u, red_part, keys, queue, total;
 };
 
 fc_status check_kv(const fc_kv_params* p) {
@@ -67,6 +67,7 @@ KvLayout kv_layout(const fc_kv_params* p) {
     L.u = o;        o = align_up(o + H * (size_t)p->d * sizeof(float));
     L.red_part = o; o = align_up(o + H * (size_t)(L.nbr > L.nkb ? L.nbr : L.nkb) * sizeof(float2));
     L.keys = o;     o = align_up(o + sel_ws_bytes(p->H, p->L_k));  // selection: keys, histograms, counts
+    L.queue = o;    o = align_up(o + kImpQueueWords * sizeof(uint32_t));  // persistent passes' counters
     L.total = o;
     return L;
 }
@@ -101,13 +102,15 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     // one plane goes straight to imp_out when the caller wants importance
     float* planes = (imp_out && L.plan.nqs == 1) ? imp_out : at<float>(ws, L.imp);
     float* u = r ? at<float>(ws, L.u) : nullptr;
+    uint32_t* queue = at<uint32_t>(ws, L.queue);
+    if (L.plan.persistent_lse || L.plan.persistent_colsum) FC_TRY(launch_imp_queue_zero(queue, s));
     // with r, redundancy pass A runs inside the pass-1 launch
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s,
-                          r ? at<float>(ws, L.u_part) : nullptr, L.nbu));
+                          r ? at<float>(ws, L.u_part) : nullptr, L.nbu, queue));
     FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s,
                                 r ? at<float>(ws, L.u_part) : nullptr, L.nbu, u, p->d));
     FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, c, s, u, r,
-                             r ? at<float2>(ws, L.red_part) : nullptr));
+                             r ? at<float2>(ws, L.red_part) : nullptr, queue + 8));
     if (imp_out && planes != imp_out) FC_TRY(launch_imp_sum_planes(planes, imp_out, p->H, p->L_k, L.plan.nqs, s));
     return FC_OK;
 }
@@ -301,7 +304,9 @@ fc_status fc_kv_importance_lse(const fc_kv_params* p, const void* Q, const void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float2* part = at<float2>(workspace, L.part);
-    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s));
+    uint32_t* queue = at<uint32_t>(workspace, L.queue);
+    if (L.plan.persistent_lse) FC_TRY(launch_imp_queue_zero(queue, s));
+    FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s, nullptr, 0, queue));
     FC_TRY(launch_imp_lse_merge(part, lse_out, nullptr, p->H, p->L_q, L.plan.nsplit, s));
     return FC_OK;
 }
@@ -318,8 +323,11 @@ fc_status fc_kv_importance_colsum(const fc_kv_params* p, const void* Q, const vo
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     float* nlse2 = at<float>(workspace, L.nlse2);
     float* planes = L.plan.nqs == 1 ? imp_out : at<float>(workspace, L.imp);
+    uint32_t* queue = at<uint32_t>(workspace, L.queue);
+    if (L.plan.persistent_colsum) FC_TRY(launch_imp_queue_zero(queue, s));
     FC_TRY(launch_imp_nlse2(lse, nlse2, p->H, p->L_q, s));
-    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s));
+    FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, log2_scale(p), s, nullptr,
+                             nullptr, nullptr, queue + 8));
     if (planes != imp_out) FC_TRY(launch_imp_sum_planes(planes, imp_out, p->H, p->L_k, L.plan.nqs, s));
     return FC_OK;
 }

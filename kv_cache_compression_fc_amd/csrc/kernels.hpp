@@ -23,14 +23,23 @@ struct ImpPlan {
     int keys_per_split;
     int nqs;
     int qtiles_per_split;
+    int slots_lse, slots_colsum;  // workgroups of each pass resident on the device at once
+    // persistent passes: one workgroup per slot taking items from per-XCD
+    // counters (queue words [0, 8) for pass 1, [8, 16) for pass 2)
+    bool persistent_lse = false, persistent_colsum = false;
 };
+constexpr int kImpQueueWords = 16;
+// Zeroes the persistent passes' counters (kImpQueueWords words).
+hipError_t launch_imp_queue_zero(uint32_t* queue, hipStream_t s);
 ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d);
 // With u_part != nullptr the same launch also runs redundancy pass A as
 // H * nbu extra workgroups: u_part[h][b] = sum of khat over key range b of
 // head h (the ranges of launch_red_norm_sum).
+// queue: the pass's 8 counters, zeroed beforehand, or nullptr (one item per
+// workgroup); used only when the plan makes the pass persistent.
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
                           int Lk, const ImpPlan& plan, float c, hipStream_t s, float* u_part = nullptr,
-                          int nbu = 0);
+                          int nbu = 0, uint32_t* queue = nullptr);
 // Queries padded to whole pass-2 tiles.
 int imp_lq_pad(int Lq);
 // Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled
@@ -45,7 +54,7 @@ int imp_colsum_blocks(int Lk);
 bool imp_grids_fit(int H, int Lq, int Lk, const ImpPlan& plan, int nbu);
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
                              int Lq, int Lk, const ImpPlan& plan, float c, hipStream_t s, const float* u = nullptr,
-                             float* r = nullptr, float2* red_part = nullptr);
+                             float* r = nullptr, float2* red_part = nullptr, uint32_t* queue = nullptr);
 // imp [H][Lk] = the sum of the nqs planes of imp_part.
 hipError_t launch_imp_sum_planes(const float* imp_part, float* imp, int H, int Lk, int nqs, hipStream_t s);
 // From the pass-1 partials: the natural-log lse [H][Lq] and/or -lse2 (either
