@@ -600,9 +600,15 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
     float pooled[kMKpt];
     if constexpr (kFromImp) {
         if (hw <= kRegHalo) {
+            // the window of this thread's 8 keys, 16 values, as four 16-byte
+            // LDS reads (kMaxHalo - kRegHalo + x0 is a multiple of 4)
             float v[kMKpt + 2 * kRegHalo];
+            const float4* w4 = reinterpret_cast<const float4*>(it + kMaxHalo - kRegHalo + x0);
 #pragma unroll
-            for (int q = 0; q < kMKpt + 2 * kRegHalo; ++q) v[q] = it[kMaxHalo - kRegHalo + x0 + q];
+            for (int q = 0; q < (kMKpt + 2 * kRegHalo) / 4; ++q) {
+                const float4 f = w4[q];
+                v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+            }
 #pragma unroll
             for (int i = 0; i < kMKpt; ++i) {
                 float p = v[kRegHalo + i];
@@ -621,11 +627,18 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
             }
         }
     }
+    uint32_t raw[kMKpt], kout[kMKpt];
+#pragma unroll
+    for (int q = 0; q < kMKpt / 4; ++q) {  // this thread's 8 values, two 16-byte LDS reads
+        const uint4 u = reinterpret_cast<const uint4*>(kt + x0)[q];
+        raw[4 * q] = u.x; raw[4 * q + 1] = u.y; raw[4 * q + 2] = u.z; raw[4 * q + 3] = u.w;
+    }
 #pragma unroll
     for (int i = 0; i < kMKpt; ++i) {
         const int x = x0 + i;
+        kout[i] = 0u;
         if (x < n) {
-            const float v = __uint_as_float(kt[x]);
+            const float v = __uint_as_float(raw[i]);
             float sc = v;
             if constexpr (kFromImp) {
                 const float red = exp2_hw(fmaf(v, kLog2e, -M)) * invS;
@@ -636,10 +649,13 @@ __global__ __launch_bounds__(kMT) void msel_keys_kernel(const float* __restrict_
                 if (red_out) red_out[j] = red;
             }
             const uint32_t key = order_key(sc);
-            kt[x] = key;  // this thread's own slot
+            kout[i] = key;
             atomicAdd(&hist[(key >> 24) * kR0Copies + copy], 1u);
         }
     }
+#pragma unroll
+    for (int q = 0; q < kMKpt / 4; ++q)  // this thread's own slots
+        reinterpret_cast<uint4*>(kt + x0)[q] = make_uint4(kout[4 * q], kout[4 * q + 1], kout[4 * q + 2], kout[4 * q + 3]);
     __syncthreads();
     uint32_t* kg = ws.keys + hL + j0;
 #pragma unroll
@@ -773,8 +789,12 @@ __global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, 
     uint32_t kv[kMKpt];
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
+    for (int q = 0; q < kMKpt / 4; ++q) {  // two 16-byte LDS reads
+        const uint4 u = reinterpret_cast<const uint4*>(kt + x0)[q];
+        kv[4 * q] = u.x; kv[4 * q + 1] = u.y; kv[4 * q + 2] = u.z; kv[4 * q + 3] = u.w;
+    }
+#pragma unroll
     for (int i = 0; i < kMKpt; ++i) {
-        kv[i] = x0 + i < n ? kt[x0 + i] : 0u;
         ngt += (x0 + i < n && kv[i] > T);
         neq += (x0 + i < n && kv[i] == T);
     }
@@ -802,11 +822,16 @@ __global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, 
 }
 
 // K_out[h][b] = K[h][idx[h][b]], V likewise: 16 bytes per lane, one row per
-// kRowBytes/16 lanes, kGatherRows output rows per block.  Rows are read and
-// written once, with non-temporal accesses.  With pos_out, the tokens'
-// positions follow them: pos_out[h][b] = pos[h][idx[h][b]].
+// kRowBytes/16 lanes, one kept row per lane group (16 rows per 256-thread
+// block for bf16 rows of 128).  Rows are read and written once, with
+// non-temporal accesses.  One 16-byte load of K and one of V per lane, in many
+// small blocks, measured faster than more loads in flight per lane (long
+// video: 182.4 -> 179.7 us for select + gather against two rows per lane
+// group; a plain streaming copy of the same bytes: 6.50 TB/s with one load per
+// lane, 6.13 with two or four).  With pos_out, the tokens' positions follow
+// them: pos_out[h][b] = pos[h][idx[h][b]].
 constexpr int kThreads = 256;
-constexpr int kGatherRows = 32;  // measured 62.6 -> 60.0 us for select + gather (MAGI-like) against 64
+template <int DT, int D> constexpr int gather_rows() { return kThreads / (D * Elem<DT>::kBytes / 16); }
 
 // kKeepAll: every row is kept (B' = L): the kernel writes idx[h][b] = b
 // itself instead of reading it.
@@ -818,49 +843,30 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int32_t* __restri
                                                                int32_t* __restrict__ pos_out) {
     constexpr int kRowBytes = D * Elem<DT>::kBytes;
     constexpr int kTpr = kRowBytes / 16;     // lanes per row
-    constexpr int kRpi = kThreads / kTpr;    // rows per step
-    constexpr int kSteps = kGatherRows / kRpi;
     const int h = blockIdx.y;
-    const int b0 = blockIdx.x * kGatherRows + threadIdx.x / kTpr;
+    const int b = blockIdx.x * gather_rows<DT, D>() + threadIdx.x / kTpr;
     const int e = threadIdx.x % kTpr;
-    const char* Ks = static_cast<const char*>(K) + (size_t)h * L * kRowBytes + e * 16;
-    const char* Vs = static_cast<const char*>(V) + (size_t)h * L * kRowBytes + e * 16;
-    char* Kd = static_cast<char*>(K_out) + (size_t)h * Bp * kRowBytes + e * 16;
-    char* Vd = static_cast<char*>(V_out) + (size_t)h * Bp * kRowBytes + e * 16;
-    int j[kSteps];
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-        const int b = b0 + i * kRpi;
-        if constexpr (kKeepAll) {
-            j[i] = b < Bp ? b : -1;
-            if (b < Bp && e == 0) idx[(size_t)h * Bp + b] = b;
-        } else {
-            j[i] = b < Bp ? idx[(size_t)h * Bp + b] : -1;
-        }
+    if (b >= Bp) return;
+    int j;
+    if constexpr (kKeepAll) {
+        j = b;
+        if (e == 0) idx[(size_t)h * Bp + b] = b;
+    } else {
+        j = idx[(size_t)h * Bp + b];
     }
-    uint4 kv[kSteps], vv[kSteps];
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-        if ((unsigned)j[i] < (unsigned)L) {
-            kv[i] = load_stream16(Ks + (size_t)j[i] * kRowBytes);
-            vv[i] = load_stream16(Vs + (size_t)j[i] * kRowBytes);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-        if ((unsigned)j[i] < (unsigned)L) {
-            const size_t b = (size_t)(b0 + i * kRpi);
-            store_stream16(Kd + b * kRowBytes, kv[i]);
-            store_stream16(Vd + b * kRowBytes, vv[i]);
-            if (pos_out != nullptr && e == 0) pos_out[(size_t)h * Bp + b] = pos[(size_t)h * L + j[i]];
-        }
-    }
+    if ((unsigned)j >= (unsigned)L) return;  // never, for indices the selection wrote
+    const uint4 kv = load_stream16(static_cast<const char*>(K) + ((size_t)h * L + j) * kRowBytes + e * 16);
+    const uint4 vv = load_stream16(static_cast<const char*>(V) + ((size_t)h * L + j) * kRowBytes + e * 16);
+    store_stream16(static_cast<char*>(K_out) + ((size_t)h * Bp + b) * kRowBytes + e * 16, kv);
+    store_stream16(static_cast<char*>(V_out) + ((size_t)h * Bp + b) * kRowBytes + e * 16, vv);
+    if (pos_out != nullptr && e == 0) pos_out[(size_t)h * Bp + b] = pos[(size_t)h * L + j];
 }
 
 template <int DT, int D>
 hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
                          void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s, int32_t* idx_keep_all) {
-    const dim3 grid((Bp + kGatherRows - 1) / kGatherRows, H);
+    constexpr int kRows = gather_rows<DT, D>();
+    const dim3 grid((Bp + kRows - 1) / kRows, H);
     if (idx_keep_all != nullptr)
         hipLaunchKernelGGL((gather_rows_kernel<DT, D, true>), grid, dim3(kThreads), 0, s, idx_keep_all, L, Bp, K, V,
                            K_out, V_out, pos, pos_out);
