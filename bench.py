@@ -152,11 +152,15 @@ def cpu_baseline(cfg, ccfg, min_seconds: float):
 
 def cache_run(fc, synth, dev, reps: int):
     """The MAGI-like cache run: chunks of 3600 tokens commit into a cache of
-    7200 per head, each compression scored by 3600 queries.  The run goes
-    through once untimed, then again with every commit timed on the stream
-    (HIP events); the compressing commits (third chunk on) are averaged.  The
-    append-only commit (copy of one chunk behind the clean rows) is timed on
-    its own for the copy kernel's bandwidth."""
+    7200 per head, each compression scored by 3600 queries.  Each chunk is
+    first written into the active rows of the cache's current region (the
+    producer's store, outside the timing), then committed in place; the run
+    goes through once untimed, then again with every commit timed on the
+    stream (HIP events), and the compressing commits (third chunk on) are
+    averaged.  The same run with the chunk handed over from its own buffer
+    (the commit copies it in first) is timed beside it, and the append-only
+    commit (copy of one chunk behind the clean rows) on its own for the copy
+    kernel's bandwidth."""
     import torch
     cfg = synth.CACHE_CONFIGS["magi"]
     log(f"generating the cache run: {cfg.n_chunks} chunks of {cfg.tokens_per_chunk} tokens, {cfg.H} heads")
@@ -166,22 +170,38 @@ def cache_run(fc, synth, dev, reps: int):
     chunks = [(K[:, c * T:(c + 1) * T].contiguous(), V[:, c * T:(c + 1) * T].contiguous()) for c in range(cfg.n_chunks)]
     del K, V
     kv = fc.KvCache(cfg.H, cfg.d, cfg.B_budget, cfg.B_active, cfg.Lq, cfg.lam, cfg.w, torch.bfloat16, device=dev)
-    for _ in range(2):  # untimed pass, then the timed one (events only; the host runs ahead)
-        kv.length, kv.next_pos = 0, 0
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.n_chunks + 1)]
-        ev[0].record()
-        for c, (Kc, Vc) in enumerate(chunks):
-            kv.commit(Kc, Vc, Q[c])
-            ev[c + 1].record()
-        torch.cuda.synchronize()
-    times = [ev[c].elapsed_time(ev[c + 1]) for c in range(cfg.n_chunks)]
-    comp = [t for c, t in enumerate(times) if (c + 1) * T > cfg.B_budget]
+
+    def run(in_place: bool):
+        times = []
+        for _ in range(2):  # untimed pass, then the timed one (events only; the host runs ahead)
+            kv.length, kv.next_pos, kv.cur = 0, 0, 0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(cfg.n_chunks)]
+            for c, (Kc, Vc) in enumerate(chunks):
+                if in_place:
+                    Ka, Va = kv.active(T)
+                    Ka.copy_(Kc)
+                    Va.copy_(Vc)
+                ev[c][0].record()
+                if in_place:
+                    kv.commit(None, None, Q[c], L_c=T)
+                else:
+                    kv.commit(Kc, Vc, Q[c])
+                ev[c][1].record()
+            torch.cuda.synchronize()
+            times = [a.elapsed_time(b) for a, b in ev]
+        return [t for c, t in enumerate(times) if (c + 1) * T > cfg.B_budget]
+
+    comp = run(True)
+    comp_copy = run(False)
     merged = cfg.B_budget + T
     commit_ms = statistics.mean(comp)
     Kc, Vc = chunks[0]
+    Bt = cfg.B_budget + cfg.B_active
 
     def append():
-        fc.fc_cache_commit(kv.p, 0, Kc, Vc, 0, None, kv.K, kv.V, kv.pos, kv.workspace)
+        fc.fc_cache_commit(kv.p, 0, Kc, Vc, 0, None, kv._K[0], kv._V[0], kv._pos[0], kv._K[1], kv._V[1], kv._pos[1],
+                           kv.workspace)
     t_app = time_events(append, reps)
     app_bytes = 2 * 2 * cfg.H * T * cfg.d * 2 + cfg.H * T * 4      # K and V rows read + written, positions
     return {
@@ -189,6 +209,9 @@ def cache_run(fc, synth, dev, reps: int):
                     f"budget {cfg.B_budget}, {cfg.Lq} queries per compression, lambda {cfg.lam}, bf16",
         "compressing_commits": len(comp), "commit_ms": commit_ms, "commit_ms_max": max(comp),
         "merged_token_heads_per_s": cfg.H * merged / (commit_ms * 1e-3),
+        "commit_with_chunk_copy_ms": statistics.mean(comp_copy),
+        "region_bytes": 2 * cfg.H * Bt * cfg.d * 2 + cfg.H * Bt * 4,
+        "workspace_bytes": int(kv.workspace.numel()),
         "append_commit_ms": t_app, "append_gbps": app_bytes / (t_app * 1e-3) / 1e9,
     }
 

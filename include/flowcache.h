@@ -212,12 +212,20 @@ fc_status fc_topb_select(int32_t H, int32_t L, int32_t B, const float* scores, i
 /* ------------------------------------------------------------------------ */
 
 /*
- * The page splits a fixed KV buffer B_total into a compressed clean region of
- * B_budget tokens and the region of the chunk being denoised (B_active).
- * When a chunk completes it enters the cache; if the clean tokens and the
- * chunk together exceed B_budget ("cache full"), the merged set is compressed
- * back to B_budget tokens per head with the joint score above; otherwise the
- * chunk is kept as it is.
+ * The page splits a fixed KV buffer of B_total = B_budget + B_active tokens
+ * per head into a compressed clean region of B_budget tokens and the region
+ * of the chunk being denoised (B_active).  When a chunk completes it enters
+ * the cache; if the clean tokens and the chunk together exceed B_budget
+ * ("cache full"), the merged set is compressed back to B_budget tokens per
+ * head with the joint score above; otherwise the chunk is kept as it is.
+ *
+ * The cache is two regions of that buffer's shape, K and V [H][B_total][d]
+ * (dtype) and positions [H][B_total] (int32, optional), all device memory:
+ * the current region and a spare.  In the current region, head h's clean
+ * tokens are rows 0..L_clean-1 in ascending position order and the chunk
+ * being denoised takes the rows right behind them.  A compressing commit
+ * reads the current region and writes the kept tokens into the spare one,
+ * which becomes the current region: the merged set is never copied.
  *
  *   H, d, lambda, pool_window, softmax_scale, dtype   as in fc_kv_params
  *   B_budget   clean tokens each head keeps
@@ -232,39 +240,48 @@ typedef struct {
 } fc_cache_params;
 
 /* Workspace bytes that fc_cache_commit needs for any commit scored by L_q
- * queries (0 if the parameters are invalid).  A commit that does not
- * compress needs no workspace. */
+ * queries (0 if the parameters are invalid): the kept indices [H][B_budget]
+ * and the compression's workspace for the largest merged set.  A commit that
+ * does not compress needs no workspace. */
 size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q);
 
 /*
  * fc_cache_commit -- a completed chunk enters the cache.
  *   L_clean          host int32 in/out: clean tokens per head before the call
  *                    (0..B_budget); after it, min(L_clean + L_c, B_budget)
- *   K_chunk, V_chunk [H][L_c][d] device, dtype: the chunk's keys and values,
- *                    1 <= L_c <= B_active
+ *   K_chunk, V_chunk [H][L_c][d] device, dtype, or both NULL: the chunk's
+ *                    keys and values, copied to rows L_clean..L_clean+L_c-1
+ *                    of the current region; NULL when the producer already
+ *                    wrote them there.  1 <= L_c <= B_active
  *   pos0             position of the chunk's first token (its tokens get
- *                    pos0, pos0 + 1, ...; pos0 >= 0, pos0 + L_c - 1 <= 2^31 - 1)
+ *                    pos0, pos0 + 1, ...; pos0 >= 0, pos0 + L_c - 1 <= 2^31 - 1),
+ *                    written to the chunk's rows of pos_cur
  *   Q [H][L_q][d]    device, dtype: the queries that score a compression;
  *                    may be NULL when the chunk fits (no compression)
- *   K_clean, V_clean [H][B_budget][d] device, dtype, in/out: the clean
- *                    region; head h's tokens are rows 0..L_clean-1 of its
- *                    B_budget rows, in ascending position order
- *   pos_clean        [H][B_budget] int32 device in/out, nullable: the
- *                    positions of the clean tokens
- * Not full (L_clean + L_c <= B_budget): the chunk's rows are copied behind
- * the clean rows.  Full: the merged set (clean rows, then the chunk) is
- * compressed as by fc_kv_compress with L_k = L_clean + L_c into the clean
- * region, and the positions follow the kept rows.  The workspace (device,
- * >= the query for this L_q) holds the merged set; it may be NULL for a
- * commit that does not compress.  K_chunk, V_chunk and Q must not overlap
- * the clean region.  *L_clean is updated when the work has been queued.
- * Errors as for fc_kv_compress; an L_clean, L_c or pos0 out of range, or a
- * NULL Q for a commit that compresses, is FC_ERR_INVALID_ARG.
+ *   K_cur, V_cur, pos_cur        the current region (pos_cur nullable)
+ *   K_spare, V_spare, pos_spare  the spare region: written only by a commit
+ *                    that compresses, and then required (pos_spare NULL
+ *                    exactly when pos_cur is)
+ *   swapped          host int32 out, nullable: 1 when the commit compressed
+ *                    and the clean tokens are now rows 0..B_budget-1 of the
+ *                    spare region (the caller swaps the two regions' roles);
+ *                    0 when they stay in the current region
+ * Not full (L_clean + L_c <= B_budget): the chunk's rows stay (or are copied)
+ * behind the clean rows.  Full: rows 0..L_clean+L_c-1 of the current region
+ * are compressed as by fc_kv_compress with L_k = L_clean + L_c, into the
+ * spare region, and the positions follow the kept rows.  The workspace
+ * (device, >= the query for this L_q) may be NULL for a commit that does not
+ * compress.  K_chunk, V_chunk and Q must not overlap either region, nor the
+ * two regions each other.  *L_clean and *swapped are set when the work has
+ * been queued.  Errors as for fc_kv_compress; an L_clean, L_c or pos0 out of
+ * range, only one of K_chunk and V_chunk, or a NULL Q or spare region for a
+ * commit that compresses, is FC_ERR_INVALID_ARG.
  */
 fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean,
                           const void* K_chunk, const void* V_chunk, int32_t L_c, int32_t pos0,
                           const void* Q, int32_t L_q,
-                          void* K_clean, void* V_clean, int32_t* pos_clean,
+                          void* K_cur, void* V_cur, int32_t* pos_cur,
+                          void* K_spare, void* V_spare, int32_t* pos_spare, int32_t* swapped,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional, Sequence
+from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
@@ -95,7 +95,8 @@ _lib.fc_cache_commit_workspace_bytes.restype = _sz
 _lib.fc_cache_commit_workspace_bytes.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.c_int32]
 _lib.fc_cache_commit.restype = ctypes.c_int
 _lib.fc_cache_commit.argtypes = [ctypes.POINTER(fc_cache_params), ctypes.POINTER(ctypes.c_int32), _vp, _vp,
-                                 ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp]
+                                 ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 ctypes.POINTER(ctypes.c_int32), _vp, _sz, _vp]
 _lib.fc_euler_step_l1_decide.restype = ctypes.c_int
 _lib.fc_euler_step_l1_decide.argtypes = [ctypes.POINTER(fc_l1_params), _i64p] + [_vp] * 8 + [_vp, _sz, _vp]
 _lib.fc_uniform_rel_l1_decide.restype = ctypes.c_int
@@ -426,32 +427,48 @@ def fc_cache_commit_workspace_bytes(c: fc_cache_params, L_q: int) -> int:
     return int(_lib.fc_cache_commit_workspace_bytes(ctypes.byref(c), int(L_q)))
 
 
-def fc_cache_commit(c: fc_cache_params, L_clean: int, K_chunk, V_chunk, pos0: int, Q, K_clean, V_clean,
-                    pos_clean=None, workspace=None, stream=None) -> int:
-    """One commit; returns the new clean length."""
+def fc_cache_commit(c: fc_cache_params, L_clean: int, K_chunk, V_chunk, pos0: int, Q, K_cur, V_cur, pos_cur=None,
+                    K_spare=None, V_spare=None, pos_spare=None, workspace=None, stream=None,
+                    L_c: Optional[int] = None) -> Tuple[int, bool]:
+    """One commit; returns (the new clean length, whether the clean tokens
+    moved to the spare region).  The regions are [H][B_budget + B_active][d]
+    (positions [H][B_budget + B_active]).  K_chunk = V_chunk = None commits
+    the L_c rows that already sit behind the clean rows of the current
+    region."""
     H, d, dt = c.H, c.d, _torch_dtype(c.dtype)
-    L_c = int(K_chunk.shape[1])
-    _expect("K_chunk", K_chunk, (H, L_c, d), dt)
-    _expect("V_chunk", V_chunk, (H, L_c, d), dt)
-    _expect("K_clean", K_clean, (H, c.B_budget, d), dt)
-    _expect("V_clean", V_clean, (H, c.B_budget, d), dt)
-    _expect("pos_clean", pos_clean, (H, c.B_budget), torch.int32)
+    Bt = c.B_budget + c.B_active
+    if K_chunk is None or V_chunk is None:
+        if K_chunk is not None or V_chunk is not None or L_c is None:
+            raise FlowCacheError("fc_cache_commit", FC_ERR_INVALID_ARG)
+        L_c = int(L_c)
+    else:
+        L_c = int(K_chunk.shape[1])
+        _expect("K_chunk", K_chunk, (H, L_c, d), dt)
+        _expect("V_chunk", V_chunk, (H, L_c, d), dt)
+    for name, t in (("K_cur", K_cur), ("V_cur", V_cur), ("K_spare", K_spare), ("V_spare", V_spare)):
+        _expect(name, t, (H, Bt, d), dt)
+    _expect("pos_cur", pos_cur, (H, Bt), torch.int32)
+    _expect("pos_spare", pos_spare, (H, Bt), torch.int32)
     if Q is not None:
         _expect("Q", Q, (H, Q.shape[1], d), dt)
     n = ctypes.c_int32(int(L_clean))
+    sw = ctypes.c_int32(0)
     L_q = int(Q.shape[1]) if Q is not None else 0
     _check("fc_cache_commit", _lib.fc_cache_commit(
-        ctypes.byref(c), ctypes.byref(n), _ptr(K_chunk), _ptr(V_chunk), int(K_chunk.shape[1]), int(pos0), _ptr(Q),
-        L_q, _ptr(K_clean), _ptr(V_clean), _ptr(pos_clean), _ptr(workspace),
+        ctypes.byref(c), ctypes.byref(n), _ptr(K_chunk), _ptr(V_chunk), L_c, int(pos0), _ptr(Q), L_q, _ptr(K_cur),
+        _ptr(V_cur), _ptr(pos_cur), _ptr(K_spare), _ptr(V_spare), _ptr(pos_spare), ctypes.byref(sw), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))
-    return int(n.value)
+    return int(n.value), bool(sw.value)
 
 
 class KvCache:
-    """A fixed-size KV cache on the device: the clean region K, V
-    [H][B_budget][d], the tokens' positions [H][B_budget] and the commit
-    workspace, allocated once.  ``commit`` adds a completed chunk (its tokens
-    take the next positions) and compresses when the budget overflows."""
+    """A fixed-size KV cache on the device: two regions of the fixed buffer
+    (K, V [H][B_budget + B_active][d], positions [H][B_budget + B_active])
+    and the commit workspace, allocated once.  ``commit`` adds a completed
+    chunk (its tokens take the next positions) and compresses when the budget
+    overflows, from the current region into the other one.  ``K``, ``V`` and
+    ``pos`` are views of the clean rows; ``active(L_c)`` gives the rows a
+    producer may write a chunk into before ``commit(None, None, Q, L_c=L_c)``."""
 
     def __init__(self, H: int, d: int, B_budget: int, B_active: int, L_q: int, lam: float, pool_window: int,
                  dtype: torch.dtype, softmax_scale: float = 0.0, device="cuda"):
@@ -460,17 +477,42 @@ class KvCache:
         nbytes = fc_cache_commit_workspace_bytes(self.p, L_q)
         if nbytes == 0:
             raise FlowCacheError("fc_cache_commit_workspace_bytes", FC_ERR_INVALID_ARG)
+        Bt = B_budget + B_active
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        self.K = torch.zeros((H, B_budget, d), dtype=dtype, device=device)
-        self.V = torch.zeros_like(self.K)
-        self.pos = torch.full((H, B_budget), -1, dtype=torch.int32, device=device)
+        self._K = [torch.zeros((H, Bt, d), dtype=dtype, device=device) for _ in range(2)]
+        self._V = [torch.zeros((H, Bt, d), dtype=dtype, device=device) for _ in range(2)]
+        self._pos = [torch.full((H, Bt), -1, dtype=torch.int32, device=device) for _ in range(2)]
+        self.cur = 0           # region holding the clean tokens
         self.length = 0        # clean tokens per head
         self.next_pos = 0      # position of the next committed token
 
-    def commit(self, K_chunk, V_chunk, Q=None, stream=None) -> int:
-        self.length = fc_cache_commit(self.p, self.length, K_chunk, V_chunk, self.next_pos, Q, self.K, self.V,
-                                      self.pos, self.workspace, stream)
-        self.next_pos += int(K_chunk.shape[1])
+    @property
+    def K(self):
+        return self._K[self.cur][:, :self.length]
+
+    @property
+    def V(self):
+        return self._V[self.cur][:, :self.length]
+
+    @property
+    def pos(self):
+        return self._pos[self.cur][:, :self.length]
+
+    def active(self, L_c: int):
+        """Views (K, V) of the L_c rows behind the clean rows of the current region."""
+        if not 1 <= L_c <= self.p.B_active:
+            raise FlowCacheError("KvCache.active", FC_ERR_INVALID_ARG)
+        return (self._K[self.cur][:, self.length:self.length + L_c],
+                self._V[self.cur][:, self.length:self.length + L_c])
+
+    def commit(self, K_chunk, V_chunk, Q=None, stream=None, L_c: Optional[int] = None) -> int:
+        c, o = self.cur, 1 - self.cur
+        self.length, swapped = fc_cache_commit(self.p, self.length, K_chunk, V_chunk, self.next_pos, Q, self._K[c],
+                                               self._V[c], self._pos[c], self._K[o], self._V[o], self._pos[o],
+                                               self.workspace, stream, L_c)
+        if swapped:
+            self.cur = o
+        self.next_pos += int(K_chunk.shape[1]) if K_chunk is not None else int(L_c)
         return self.length
 
 

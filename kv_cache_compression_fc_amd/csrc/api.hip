@@ -94,7 +94,7 @@ fc_status hip_status(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_HIP
 // the second pass produces the redundancy of the keys it holds and the
 // softmax partials of r, one per key block.
 fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, float* imp_out,
-                         void* ws, hipStream_t s, float* r = nullptr) {
+                         void* ws, hipStream_t s, float* r = nullptr, int ldk = 0) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const float c = log2_scale(p);
     float2* part = at<float2>(ws, L.part);
@@ -106,27 +106,29 @@ fc_status run_importance(const fc_kv_params* p, const KvLayout& L, const void* Q
     if (L.plan.persistent_lse || L.plan.persistent_colsum) FC_TRY(launch_imp_queue_zero(queue, s));
     // with r, redundancy pass A runs inside the pass-1 launch
     FC_TRY(launch_imp_lse(dt, p->d, Q, K, part, p->H, p->L_q, p->L_k, L.plan, c, s,
-                          r ? at<float>(ws, L.u_part) : nullptr, L.nbu, queue));
+                          r ? at<float>(ws, L.u_part) : nullptr, L.nbu, queue, ldk));
     FC_TRY(launch_imp_lse_merge(part, nullptr, nlse2, p->H, p->L_q, L.plan.nsplit, s,
                                 r ? at<float>(ws, L.u_part) : nullptr, L.nbu, u, p->d));
     FC_TRY(launch_imp_colsum(dt, p->d, Q, K, nlse2, planes, p->H, p->L_q, p->L_k, L.plan, c, s, u, r,
-                             r ? at<float2>(ws, L.red_part) : nullptr, queue + 8));
+                             r ? at<float2>(ws, L.red_part) : nullptr, queue + 8, ldk));
     if (imp_out && planes != imp_out) FC_TRY(launch_imp_sum_planes(planes, imp_out, p->H, p->L_k, L.plan.nqs, s));
     return FC_OK;
 }
 
 // The whole compression of K, V [H][L_k][d] into K_out, V_out [H][B'][d]
 // (arguments already checked).  With pos_out the positions pos [H][L_k]
-// follow the kept rows.
+// follow the kept rows.  Head strides in rows: ld_in for K, V and pos, ld_out
+// for K_out, V_out and pos_out (0: dense, L_k and B').
 fc_status kv_compress_run(const fc_kv_params* p, const KvLayout& L, const void* Q, const void* K, const void* V,
                           void* K_out, void* V_out, int32_t* idx_out, float* score_out, float* imp_pooled_out,
                           float* red_out, void* ws, hipStream_t s, const int32_t* pos = nullptr,
-                          int32_t* pos_out = nullptr) {
+                          int32_t* pos_out = nullptr, int ld_in = 0, int ld_out = 0) {
     const int dt = p->dtype == FC_BF16 ? kBF16 : kF32;
     const int Bp = p->B_budget < p->L_k ? p->B_budget : p->L_k;
     if (Bp == p->L_k && !score_out && !imp_pooled_out && !red_out) {
         // every token is kept and no score is asked for: the rows are copied
-        FC_TRY(launch_gather(dt, p->d, nullptr, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out, idx_out));
+        FC_TRY(launch_gather(dt, p->d, nullptr, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out, idx_out, ld_in,
+                             ld_out));
         return FC_OK;
     }
     float* imp = at<float>(ws, L.imp);
@@ -134,12 +136,13 @@ fc_status kv_compress_run(const fc_kv_params* p, const KvLayout& L, const void* 
     float2* red_part = at<float2>(ws, L.red_part);
     // importance (planes in the workspace): its first launch also runs
     // redundancy pass A, its second pass forms r and the softmax partials of r
-    const fc_status st = run_importance(p, L, Q, K, nullptr, ws, s, r);
+    const fc_status st = run_importance(p, L, Q, K, nullptr, ws, s, r, ld_in);
     if (st != FC_OK) return st;
     // pool + score + top-B + gather
     FC_TRY(launch_sel_head(imp, L.plan.nqs, r, red_part, L.nkb, p->lambda, p->pool_window, score_out, imp_pooled_out,
                            red_out, at<uint32_t>(ws, L.keys), p->H, p->L_k, Bp, idx_out, s));
-    FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out));
+    FC_TRY(launch_gather(dt, p->d, idx_out, p->H, p->L_k, Bp, K, V, K_out, V_out, s, pos, pos_out, nullptr, ld_in,
+                         ld_out));
     return FC_OK;
 }
 
@@ -166,21 +169,15 @@ fc_kv_params cache_kv_params(const fc_cache_params* c, int32_t L_q, int32_t L) {
     return p;
 }
 
-// Workspace of a compressing commit: the merged set (K, V, positions), the
-// kept indices, then the compression's own workspace.
+// Workspace of a compressing commit: the kept indices, then the
+// compression's own workspace.
 struct CacheLayout {
-    size_t Km, Vm, pm, idx, comp;
+    size_t idx, comp;
 };
 CacheLayout cache_layout(const fc_cache_params* c) {
-    const size_t H = (size_t)c->H, Bt = (size_t)c->B_budget + (size_t)c->B_active;
-    const size_t row = (size_t)c->d * (c->dtype == FC_BF16 ? 2 : 4);
     CacheLayout L{};
-    size_t o = 0;
-    L.Km = o;   o = align_up(o + H * Bt * row);
-    L.Vm = o;   o = align_up(o + H * Bt * row);
-    L.pm = o;   o = align_up(o + H * Bt * sizeof(int32_t));
-    L.idx = o;  o = align_up(o + H * (size_t)c->B_budget * sizeof(int32_t));
-    L.comp = o;
+    L.idx = 0;
+    L.comp = align_up((size_t)c->H * (size_t)c->B_budget * sizeof(int32_t));
     return L;
 }
 
@@ -410,45 +407,50 @@ size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q) {
 }
 
 fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void* K_chunk, const void* V_chunk,
-                          int32_t L_c, int32_t pos0, const void* Q, int32_t L_q, void* K_clean, void* V_clean,
-                          int32_t* pos_clean, void* workspace, size_t workspace_bytes, void* stream) {
+                          int32_t L_c, int32_t pos0, const void* Q, int32_t L_q, void* K_cur, void* V_cur,
+                          int32_t* pos_cur, void* K_spare, void* V_spare, int32_t* pos_spare, int32_t* swapped,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     fc_status st = check_cache(c);
     if (st != FC_OK) return st;
     if (L_clean == nullptr || *L_clean < 0 || *L_clean > c->B_budget) return FC_ERR_INVALID_ARG;
     if (L_c < 1 || L_c > c->B_active || pos0 < 0 || (long long)pos0 + L_c - 1 > 0x7fffffffLL) return FC_ERR_INVALID_ARG;
-    if (!K_chunk || !V_chunk || !K_clean || !V_clean) return FC_ERR_INVALID_ARG;
-    if (!aligned16(K_chunk) || !aligned16(V_chunk) || !aligned16(K_clean) || !aligned16(V_clean))
-        return FC_ERR_INVALID_ARG;
+    if (!K_cur || !V_cur || !aligned16(K_cur) || !aligned16(V_cur)) return FC_ERR_INVALID_ARG;
+    if ((K_chunk == nullptr) != (V_chunk == nullptr)) return FC_ERR_INVALID_ARG;
+    if (K_chunk && (!aligned16(K_chunk) || !aligned16(V_chunk))) return FC_ERR_INVALID_ARG;
     const int32_t n_old = *L_clean, L = n_old + L_c;
+    const int32_t ld = c->B_budget + c->B_active;  // rows per head of either region
     // the compression's checks (head dim, dtype, lambda, window, scale, sizes)
     // apply to every commit, so that an invalid cache fails on its first call
     const fc_kv_params kp = cache_kv_params(c, L_q > 0 ? L_q : 1, L);
     st = check_kv(&kp);
     if (st != FC_OK) return st;
+    const bool full = L > c->B_budget;
+    if (full) {
+        if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
+        if (!K_spare || !V_spare || !aligned16(K_spare) || !aligned16(V_spare)) return FC_ERR_INVALID_ARG;
+        if ((pos_cur == nullptr) != (pos_spare == nullptr)) return FC_ERR_INVALID_ARG;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = c->dtype == FC_BF16 ? kBF16 : kF32;
-    if (L <= c->B_budget) {
+    if (!full) {
         // not full: the chunk is kept as it is, behind the clean tokens
-        FC_TRY(launch_cache_rows(dt, c->d, c->H, nullptr, nullptr, nullptr, 0, 0, K_chunk, V_chunk, L_c, pos0,
-                                 K_clean, V_clean, pos_clean, c->B_budget, n_old, s));
+        FC_TRY(launch_cache_append(dt, c->d, c->H, K_chunk, V_chunk, L_c, pos0, K_cur, V_cur, pos_cur, ld, n_old, s));
         *L_clean = L;
+        if (swapped) *swapped = 0;
         return FC_OK;
     }
-    // full: merge, then keep the top-B_budget tokens of the merged set per head
-    if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
+    // full: the clean rows and the chunk behind them are one row range of the
+    // current region; its top-B_budget tokens per head go to the spare region
     const CacheLayout CL = cache_layout(c);
     const KvLayout KL = kv_layout(&kp);
     if (!KL.fits) return FC_ERR_UNSUPPORTED;
     if (!ws_ok(workspace, workspace_bytes, CL.comp + KL.total)) return FC_ERR_WORKSPACE;
-    void* Km = at<char>(workspace, CL.Km);
-    void* Vm = at<char>(workspace, CL.Vm);
-    int32_t* pm = pos_clean ? at<int32_t>(workspace, CL.pm) : nullptr;
-    FC_TRY(launch_cache_rows(dt, c->d, c->H, K_clean, V_clean, pos_clean, c->B_budget, n_old, K_chunk, V_chunk, L_c,
-                             pos0, Km, Vm, pm, L, 0, s));
-    st = kv_compress_run(&kp, KL, Q, Km, Vm, K_clean, V_clean, at<int32_t>(workspace, CL.idx), nullptr, nullptr,
-                         nullptr, at<char>(workspace, CL.comp), s, pm, pos_clean);
+    FC_TRY(launch_cache_append(dt, c->d, c->H, K_chunk, V_chunk, L_c, pos0, K_cur, V_cur, pos_cur, ld, n_old, s));
+    st = kv_compress_run(&kp, KL, Q, K_cur, V_cur, K_spare, V_spare, at<int32_t>(workspace, CL.idx), nullptr, nullptr,
+                         nullptr, at<char>(workspace, CL.comp), s, pos_cur, pos_spare, ld, ld);
     if (st != FC_OK) return st;
     *L_clean = c->B_budget;
+    if (swapped) *swapped = 1;
     return FC_OK;
 }
 

@@ -234,7 +234,8 @@ template <int DT, int D, bool kPersist>
 __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_kernel(const void* __restrict__ Q,
                                                                             const void* __restrict__ K,
                                                                             float2* __restrict__ part, int Lq,
-                                                                            int Lk, int keys_per_split, int nsplit,
+                                                                            int Lk, int ldk, int keys_per_split,
+                                                                            int nsplit,
                                                                             int nqb, int n_items, float c,
                                                                             float* __restrict__ u_part, int nbu,
                                                                             int n_lse_blocks,
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         const int h = b / nbu, blk = b % nbu;
         const int rows = (Lk + nbu - 1) / nbu;
         const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
-        red_norm_sum_rows<DT, D, kThreads>(static_cast<const char*>(K) + (size_t)h * Lk * D * kE, r0, r1,
+        red_norm_sum_rows<DT, D, kThreads>(static_cast<const char*>(K) + (size_t)h * ldk * D * kE, r0, r1,
                                            reinterpret_cast<float*>(lds0), u_part + ((size_t)h * nbu + blk) * D);
     };
     auto run_lse = [&](const int item) {
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         // and waits stay the same on all waves.
         const bool live = qblk * kRowsPerBlock + wave * 32 < Lq;
         const char* Qh = static_cast<const char*>(Q) + (size_t)h * Lq * D * kE;
-        const __amdgpu_buffer_rsrc_t krs = head_rsrc(static_cast<const char*>(K) + (size_t)h * Lk * D * kE,
+        const __amdgpu_buffer_rsrc_t krs = head_rsrc(static_cast<const char*>(K) + (size_t)h * ldk * D * kE,
                                                      (uint32_t)Lk * D * kE);
 
         const int k_begin = split * keys_per_split;
@@ -590,7 +591,8 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
                                                                                const void* __restrict__ K,
                                                                                const float* __restrict__ nlse2,
                                                                                float* __restrict__ imp, int H,
-                                                                               int Lq, int lq_pad, int Lk, int nkb,
+                                                                               int Lq, int lq_pad, int Lk, int ldk,
+                                                                               int nkb,
                                                                                int nqs, int tpi, int n_items,
                                                                                float c, float inv_lq,
                                                                                const float* __restrict__ u,
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         const __amdgpu_buffer_rsrc_t qrs = head_rsrc(static_cast<const char*>(Q) + (size_t)h * Lq * D * kE,
                                                      (uint32_t)Lq * D * kE);
         const __amdgpu_buffer_rsrc_t nrs = head_rsrc(nlse2 + (size_t)h * lq_pad, (uint32_t)lq_pad * 4);
-        const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
+        const char* Kh = static_cast<const char*>(K) + (size_t)h * ldk * D * kE;
         // this item's query tiles [t_begin, t_end)
         const int t_begin = qs * tpi;
         const int t_end = min((Lq + QT - 1) / QT, t_begin + tpi);
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
 
 template <int DT, int D>
 hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq, int Lk, const ImpPlan& p,
-                      float c, hipStream_t s, float* u_part, int nbu, uint32_t* queue) {
+                      float c, hipStream_t s, float* u_part, int nbu, uint32_t* queue, int ldk) {
     static_assert(kThreads / kWave * D * 4 <= SwizzledTile<DT, D, tile_rows<DT>()>::kBytes,
                   "redundancy scratch must fit in one tile buffer");
     const int nqb = (Lq + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -749,11 +751,11 @@ hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq,
     const int red_blocks = u_part != nullptr ? H * nbu : 0;
     if (queue != nullptr && p.persistent_lse)  // one workgroup per slot
         hipLaunchKernelGGL((imp_lse_kernel<DT, D, true>), dim3(p.slots_lse / 8 * 8), dim3(kThreads), 0, s, Q, K,
-                           part, Lq, Lk, p.keys_per_split, p.nsplit, nqb, (int)n_items, c, u_part, nbu, lse_blocks,
+                           part, Lq, Lk, ldk, p.keys_per_split, p.nsplit, nqb, (int)n_items, c, u_part, nbu, lse_blocks,
                            queue, H);
     else
         hipLaunchKernelGGL((imp_lse_kernel<DT, D, false>), dim3(lse_blocks + red_blocks), dim3(kThreads), 0, s, Q, K,
-                           part, Lq, Lk, p.keys_per_split, p.nsplit, nqb, (int)n_items, c, u_part, nbu, lse_blocks,
+                           part, Lq, Lk, ldk, p.keys_per_split, p.nsplit, nqb, (int)n_items, c, u_part, nbu, lse_blocks,
                            nullptr, H);
     return hipGetLastError();
 }
@@ -761,17 +763,17 @@ hipError_t lse_launch(const void* Q, const void* K, float2* part, int H, int Lq,
 template <int DT, int D>
 hipError_t colsum_launch(const void* Q, const void* K, const float* nlse2, float* imp_part, int H, int Lq, int Lk,
                          const ImpPlan& p, float c, hipStream_t s, const float* u, float* r, float2* red_part,
-                         uint32_t* queue) {
+                         uint32_t* queue, int ldk) {
     const int nkb = (Lk + kRowsPerBlock - 1) / kRowsPerBlock;
     const long long n_items = (long long)H * p.nqs * nkb;
     const int blocks = (int)((n_items + 7) / 8 * 8);
     if (queue != nullptr && p.persistent_colsum)  // one workgroup per slot
         hipLaunchKernelGGL((imp_colsum_kernel<DT, D, true>), dim3(p.slots_colsum / 8 * 8), dim3(kThreads), 0, s, Q,
-                           K, nlse2, imp_part, H, Lq, imp_lq_pad(Lq), Lk, nkb, p.nqs, p.qtiles_per_split, (int)n_items,
+                           K, nlse2, imp_part, H, Lq, imp_lq_pad(Lq), Lk, ldk, nkb, p.nqs, p.qtiles_per_split, (int)n_items,
                            c, 1.0f / (float)Lq, u, r, red_part, queue);
     else
         hipLaunchKernelGGL((imp_colsum_kernel<DT, D, false>), dim3(blocks), dim3(kThreads), 0, s, Q, K, nlse2,
-                           imp_part, H, Lq, imp_lq_pad(Lq), Lk, nkb, p.nqs, p.qtiles_per_split, (int)n_items, c,
+                           imp_part, H, Lq, imp_lq_pad(Lq), Lk, ldk, nkb, p.nqs, p.qtiles_per_split, (int)n_items, c,
                            1.0f / (float)Lq, u, r, red_part, nullptr);
     return hipGetLastError();
 }
@@ -890,11 +892,14 @@ ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d) {
 }
 
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq, int Lk,
-                          const ImpPlan& plan, float c, hipStream_t s, float* u_part, int nbu, uint32_t* queue) {
-    if (dt == kBF16) return d == 128 ? lse_launch<kBF16, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue)
-                                     : lse_launch<kBF16, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue);
-    return d == 128 ? lse_launch<kF32, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue)
-                    : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue);
+                          const ImpPlan& plan, float c, hipStream_t s, float* u_part, int nbu, uint32_t* queue,
+                          int ldk) {
+    if (ldk < Lk) ldk = Lk;
+    if (dt == kBF16)
+        return d == 128 ? lse_launch<kBF16, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue, ldk)
+                        : lse_launch<kBF16, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue, ldk);
+    return d == 128 ? lse_launch<kF32, 128>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue, ldk)
+                    : lse_launch<kF32, 64>(Q, K, part, H, Lq, Lk, plan, c, s, u_part, nbu, queue, ldk);
 }
 
 int imp_colsum_blocks(int Lk) { return (Lk + kRowsPerBlock - 1) / kRowsPerBlock; }
@@ -909,12 +914,14 @@ bool imp_grids_fit(int H, int Lq, int Lk, const ImpPlan& p, int nbu) {
 
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
                              int Lq, int Lk, const ImpPlan& p, float c, hipStream_t s, const float* u, float* r,
-                             float2* red_part, uint32_t* queue) {
+                             float2* red_part, uint32_t* queue, int ldk) {
+    if (ldk < Lk) ldk = Lk;
     if (dt == kBF16)
-        return d == 128 ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue)
-                        : colsum_launch<kBF16, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue);
-    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue)
-                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue);
+        return d == 128
+                   ? colsum_launch<kBF16, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue, ldk)
+                   : colsum_launch<kBF16, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue, ldk);
+    return d == 128 ? colsum_launch<kF32, 128>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue, ldk)
+                    : colsum_launch<kF32, 64>(Q, K, nlse2, imp_part, H, Lq, Lk, p, c, s, u, r, red_part, queue, ldk);
 }
 
 hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, int H, int Lq, int nsplit,

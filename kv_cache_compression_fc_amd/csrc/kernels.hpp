@@ -37,9 +37,11 @@ ImpPlan imp_plan(int H, int Lq, int Lk, int dt, int d);
 // head h (the ranges of launch_red_norm_sum).
 // queue: the pass's 8 counters, zeroed beforehand, or nullptr (one item per
 // workgroup); used only when the plan makes the pass persistent.
+// ldk: rows per head in K (head h starts at row h * ldk); values below Lk
+// mean dense (Lk).  The same for launch_imp_colsum.
 hipError_t launch_imp_lse(int dt, int d, const void* Q, const void* K, float2* part, int H, int Lq,
                           int Lk, const ImpPlan& plan, float c, hipStream_t s, float* u_part = nullptr,
-                          int nbu = 0, uint32_t* queue = nullptr);
+                          int nbu = 0, uint32_t* queue = nullptr, int ldk = 0);
 // Queries padded to whole pass-2 tiles.
 int imp_lq_pad(int Lq);
 // Pass 2 from -lse2 [H][imp_lq_pad(Lq)] (base-2 log-sum-exp of the scaled
@@ -54,7 +56,8 @@ int imp_colsum_blocks(int Lk);
 bool imp_grids_fit(int H, int Lq, int Lk, const ImpPlan& plan, int nbu);
 hipError_t launch_imp_colsum(int dt, int d, const void* Q, const void* K, const float* nlse2, float* imp_part, int H,
                              int Lq, int Lk, const ImpPlan& plan, float c, hipStream_t s, const float* u = nullptr,
-                             float* r = nullptr, float2* red_part = nullptr, uint32_t* queue = nullptr);
+                             float* r = nullptr, float2* red_part = nullptr, uint32_t* queue = nullptr,
+                             int ldk = 0);
 // imp [H][Lk] = the sum of the nqs planes of imp_part.
 hipError_t launch_imp_sum_planes(const float* imp_part, float* imp, int H, int Lk, int nqs, hipStream_t s);
 // From the pass-1 partials: the natural-log lse [H][Lq] and/or -lse2 (either
@@ -94,19 +97,20 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
 // K_out[h][b] = K[h][idx[h][b]], V likewise; with pos_out also
 // pos_out[h][b] = pos[h][idx[h][b]] (pos [H][L], pos_out [H][Bp]).  With
 // idx_keep_all (Bp == L) every row is kept: idx is not read, and
-// idx_keep_all[h][b] = b is written.
+// idx_keep_all[h][b] = b is written.  Head strides in rows: ld_in for K, V
+// and pos, ld_out for K_out, V_out and pos_out (values below L and Bp mean
+// dense: L and Bp).
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
                          void* K_out, void* V_out, hipStream_t s, const int32_t* pos = nullptr,
-                         int32_t* pos_out = nullptr, int32_t* idx_keep_all = nullptr);
+                         int32_t* pos_out = nullptr, int32_t* idx_keep_all = nullptr, int ld_in = 0,
+                         int ld_out = 0);
 
 // ---- KV cache manager -----------------------------------------------------------
-// dst[h][row0 + j] = j < n_old ? old[h][j] : fresh[h][j - n_old] for K and V,
-// 0 <= j < n_old + n_new, head strides ld_old / n_new / ld_dst rows; with
-// pos_dst also the positions (pos_old[h][j] for old rows, pos0 + j - n_old
-// for fresh ones).
-hipError_t launch_cache_rows(int dt, int d, int H, const void* K_old, const void* V_old, const int32_t* pos_old,
-                             int ld_old, int n_old, const void* K_new, const void* V_new, int n_new, int32_t pos0,
-                             void* K_dst, void* V_dst, int32_t* pos_dst, int ld_dst, int row0, hipStream_t s);
+// dst[h][row0 + j] = fresh[h][j] for K and V, 0 <= j < n_new (skipped when
+// K_new is null), head strides n_new / ld_dst rows; with pos_dst also
+// pos_dst[h][row0 + j] = pos0 + j.
+hipError_t launch_cache_append(int dt, int d, int H, const void* K_new, const void* V_new, int n_new, int32_t pos0,
+                               void* K_dst, void* V_dst, int32_t* pos_dst, int ld_dst, int row0, hipStream_t s);
 
 // ---- chunk relative L1 ------------------------------------------------------
 constexpr int kMaxChunks = 128;

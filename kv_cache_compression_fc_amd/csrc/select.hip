@@ -829,7 +829,9 @@ __global__ __launch_bounds__(kMT) void msel_compact_kernel(int H, int L, int G, 
 // video: 182.4 -> 179.7 us for select + gather against two rows per lane
 // group; a plain streaming copy of the same bytes: 6.50 TB/s with one load per
 // lane, 6.13 with two or four).  With pos_out, the tokens' positions follow
-// them: pos_out[h][b] = pos[h][idx[h][b]].
+// them: pos_out[h][b] = pos[h][idx[h][b]].  Head strides: ld_in rows for K, V
+// and pos, ld_out rows for K_out, V_out and pos_out (L and Bp when the
+// tensors are dense).
 constexpr int kThreads = 256;
 template <int DT, int D> constexpr int gather_rows() { return kThreads / (D * Elem<DT>::kBytes / 16); }
 
@@ -840,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int32_t* __restri
                                                                const void* __restrict__ K, const void* __restrict__ V,
                                                                void* __restrict__ K_out, void* __restrict__ V_out,
                                                                const int32_t* __restrict__ pos,
-                                                               int32_t* __restrict__ pos_out) {
+                                                               int32_t* __restrict__ pos_out, int ld_in, int ld_out) {
     constexpr int kRowBytes = D * Elem<DT>::kBytes;
     constexpr int kTpr = kRowBytes / 16;     // lanes per row
     const int h = blockIdx.y;
@@ -855,24 +857,26 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int32_t* __restri
         j = idx[(size_t)h * Bp + b];
     }
     if ((unsigned)j >= (unsigned)L) return;  // never, for indices the selection wrote
-    const uint4 kv = load_stream16(static_cast<const char*>(K) + ((size_t)h * L + j) * kRowBytes + e * 16);
-    const uint4 vv = load_stream16(static_cast<const char*>(V) + ((size_t)h * L + j) * kRowBytes + e * 16);
-    store_stream16(static_cast<char*>(K_out) + ((size_t)h * Bp + b) * kRowBytes + e * 16, kv);
-    store_stream16(static_cast<char*>(V_out) + ((size_t)h * Bp + b) * kRowBytes + e * 16, vv);
-    if (pos_out != nullptr && e == 0) pos_out[(size_t)h * Bp + b] = pos[(size_t)h * L + j];
+    const size_t src = (size_t)h * ld_in + j, dst = (size_t)h * ld_out + b;
+    const uint4 kv = load_stream16(static_cast<const char*>(K) + src * kRowBytes + e * 16);
+    const uint4 vv = load_stream16(static_cast<const char*>(V) + src * kRowBytes + e * 16);
+    store_stream16(static_cast<char*>(K_out) + dst * kRowBytes + e * 16, kv);
+    store_stream16(static_cast<char*>(V_out) + dst * kRowBytes + e * 16, vv);
+    if (pos_out != nullptr && e == 0) pos_out[dst] = pos[src];
 }
 
 template <int DT, int D>
 hipError_t gather_launch(const int32_t* idx, int H, int L, int Bp, const void* K, const void* V, void* K_out,
-                         void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s, int32_t* idx_keep_all) {
+                         void* V_out, const int32_t* pos, int32_t* pos_out, hipStream_t s, int32_t* idx_keep_all,
+                         int ld_in, int ld_out) {
     constexpr int kRows = gather_rows<DT, D>();
     const dim3 grid((Bp + kRows - 1) / kRows, H);
     if (idx_keep_all != nullptr)
         hipLaunchKernelGGL((gather_rows_kernel<DT, D, true>), grid, dim3(kThreads), 0, s, idx_keep_all, L, Bp, K, V,
-                           K_out, V_out, pos, pos_out);
+                           K_out, V_out, pos, pos_out, ld_in, ld_out);
     else
         hipLaunchKernelGGL((gather_rows_kernel<DT, D, false>), grid, dim3(kThreads), 0, s, const_cast<int32_t*>(idx),
-                           L, Bp, K, V, K_out, V_out, pos, pos_out);
+                           L, Bp, K, V, K_out, V_out, pos, pos_out, ld_in, ld_out);
     return hipGetLastError();
 }
 
@@ -979,12 +983,14 @@ hipError_t launch_sel_head(const float* src, int nsrc, const float* r, const flo
 
 hipError_t launch_gather(int dt, int d, const int32_t* idx, int H, int L, int Bp, const void* K, const void* V,
                          void* K_out, void* V_out, hipStream_t s, const int32_t* pos, int32_t* pos_out,
-                         int32_t* idx_keep_all) {
-    if (dt == kBF16)
-        return d == 128 ? gather_launch<kBF16, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all)
-                        : gather_launch<kBF16, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all);
-    return d == 128 ? gather_launch<kF32, 128>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all)
-                    : gather_launch<kF32, 64>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all);
+                         int32_t* idx_keep_all, int ld_in, int ld_out) {
+    if (ld_in < L) ld_in = L;
+    if (ld_out < Bp) ld_out = Bp;
+#define FC_GATHER(DT_, D_) \
+    gather_launch<DT_, D_>(idx, H, L, Bp, K, V, K_out, V_out, pos, pos_out, s, idx_keep_all, ld_in, ld_out)
+    if (dt == kBF16) return d == 128 ? FC_GATHER(kBF16, 128) : FC_GATHER(kBF16, 64);
+    return d == 128 ? FC_GATHER(kF32, 128) : FC_GATHER(kF32, 64);
+#undef FC_GATHER
 }
 
 }  // namespace fc

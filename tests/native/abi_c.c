@@ -43,8 +43,10 @@ int main(void) {
     fc_cache_params c = {24, 128, 7200, 3600, 0.5f, 7, 0.0f, FC_BF16};
     CHECK(fc_cache_commit_workspace_bytes(&c, 3600) > 0);
     int32_t L_clean = 7201;
-    CHECK(fc_cache_commit(&c, &L_clean, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, NULL, NULL, 0, NULL) ==
-          FC_ERR_INVALID_ARG);
+    int32_t swapped = -1;
+    CHECK(fc_cache_commit(&c, &L_clean, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, NULL, dummy, dummy, NULL,
+                          &swapped, NULL, 0, NULL) == FC_ERR_INVALID_ARG);
+    CHECK(swapped == -1);
 
     printf("%s\n", fails ? "C ABI checks failed" : "C ABI checks ok");
     return fails != 0;

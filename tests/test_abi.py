@@ -136,11 +136,12 @@ def _cache_params(fc, **kw):
 def test_cache_workspace_query(fc):
     c = _cache_params(fc)
     n = fc.fc_cache_commit_workspace_bytes(c, 3600)
-    # the merged set (K, V rows and positions of B_total tokens) plus a
-    # compression of the largest merged set
-    merged = 2 * 24 * 10800 * 128 * 2 + 24 * 10800 * 4
-    kp = fc.fc_kv_params(24, 128, 3600, 10800, 7200, 0.5, 7, 0.0, fc.FC_BF16)
-    assert n >= merged + fc.fc_kv_compress_workspace_bytes(kp)
+    # the kept indices plus the compression's workspace for every merged
+    # length B_budget < L <= B_total (no merged copy of K and V)
+    idx = 24 * 7200 * 4
+    comp = [fc.fc_kv_compress_workspace_bytes(fc.fc_kv_params(24, 128, 3600, L, 7200, 0.5, 7, 0.0, fc.FC_BF16))
+            for L in range(7201, 10801)]
+    assert n == (idx + 255) // 256 * 256 + max(comp)
     assert n % 256 == 0
     for bad in (dict(H=0), dict(B_budget=0), dict(B_active=0), dict(lambda_=-0.1), dict(pool_window=2),
                 dict(d=80), dict(dtype=5), dict(B_budget=2 ** 31 - 10, B_active=100)):
@@ -154,10 +155,13 @@ def test_cache_argument_errors(fc):
     dummy = ctypes.c_void_p(4096)
     need = fc.fc_cache_commit_workspace_bytes(c, 3600)
 
-    def commit(L_clean, L_c, pos0=0, Q=dummy, ws_bytes=need, p=c, K_chunk=dummy):
+    def commit(L_clean, L_c, pos0=0, Q=dummy, ws_bytes=need, p=c, K_chunk=dummy, V_chunk=dummy, K_spare=dummy,
+               pos_cur=dummy, pos_spare=dummy):
         n = ctypes.c_int32(L_clean)
-        st = lib.fc_cache_commit(ctypes.byref(p), ctypes.byref(n), K_chunk, dummy, L_c, pos0, Q, 3600, dummy,
-                                 dummy, dummy, dummy, ws_bytes, None)
+        sw = ctypes.c_int32(-7)
+        st = lib.fc_cache_commit(ctypes.byref(p), ctypes.byref(n), K_chunk, V_chunk, L_c, pos0, Q, 3600, dummy,
+                                 dummy, pos_cur, K_spare, dummy, pos_spare, ctypes.byref(sw), dummy, ws_bytes, None)
+        assert sw.value == -7  # untouched on error
         return st, n.value
 
     assert commit(-1, 100) == (fc.FC_ERR_INVALID_ARG, -1)
@@ -172,8 +176,14 @@ def test_cache_argument_errors(fc):
     # a commit that overflows the budget needs queries and the workspace
     assert commit(7200, 100, Q=None) == (fc.FC_ERR_INVALID_ARG, 7200)
     assert commit(7200, 100, ws_bytes=need // 2) == (fc.FC_ERR_WORKSPACE, 7200)
+    # ... and the spare region, with positions on both sides or neither
+    assert commit(7200, 100, K_spare=None) == (fc.FC_ERR_INVALID_ARG, 7200)
+    assert commit(7200, 100, pos_spare=None) == (fc.FC_ERR_INVALID_ARG, 7200)
+    assert commit(7200, 100, K_spare=ctypes.c_void_p(4100)) == (fc.FC_ERR_INVALID_ARG, 7200)
+    # a chunk given by one pointer only
+    assert commit(0, 100, V_chunk=None) == (fc.FC_ERR_INVALID_ARG, 0)
     assert lib.fc_cache_commit(ctypes.byref(c), None, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, dummy, dummy,
-                               need, None) == fc.FC_ERR_INVALID_ARG
+                               dummy, dummy, None, dummy, need, None) == fc.FC_ERR_INVALID_ARG
 
 
 def test_binding_refuses_mismatched_tensors(fc):
@@ -227,17 +237,20 @@ def test_binding_refuses_mismatched_tensors(fc):
         fc.fc_uniform_rel_l1_decide(p, offs, x, x, st, st[:1], f, rec, workspace=ws)
 
     c = fc.fc_cache_params(2, 64, 32, 16, 0.5, 3, 0.0, fc.FC_BF16)
-    Kc = torch.zeros(2, 32, 64, dtype=bf)
-    pos = torch.zeros(2, 32, dtype=torch.int32)
+    Kc = torch.zeros(2, 48, 64, dtype=bf)
+    pos = torch.zeros(2, 48, dtype=torch.int32)
+    K8 = torch.zeros(2, 8, 64, dtype=bf)
     with pytest.raises(ValueError, match="K_chunk: shape"):
         fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 128, dtype=bf), torch.zeros(2, 8, 128, dtype=bf), 0, None, Kc,
-                           Kc, pos, ws)
-    with pytest.raises(ValueError, match="pos_clean: dtype"):
-        fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 8, 64, dtype=bf), 0, None, Kc, Kc,
-                           pos.long(), ws)
+                           Kc, pos, Kc, Kc, pos, ws)
+    with pytest.raises(ValueError, match="K_cur: shape"):   # regions hold B_budget + B_active rows
+        fc.fc_cache_commit(c, 0, K8, K8, 0, None, Kc[:, :32], Kc, pos, Kc, Kc, pos, ws)
+    with pytest.raises(ValueError, match="pos_spare: dtype"):
+        fc.fc_cache_commit(c, 0, K8, K8, 0, None, Kc, Kc, pos, Kc, Kc, pos.long(), ws)
+    with pytest.raises(fc.FlowCacheError):   # an in-place chunk needs its length
+        fc.fc_cache_commit(c, 0, None, None, 0, None, Kc, Kc, pos, Kc, Kc, pos, ws)
     with pytest.raises(ValueError, match="on the GPU"):  # consistent arguments reach the device check
-        fc.fc_cache_commit(c, 0, torch.zeros(2, 8, 64, dtype=bf), torch.zeros(2, 8, 64, dtype=bf), 0, None, Kc, Kc,
-                           pos, ws)
+        fc.fc_cache_commit(c, 0, K8, K8, 0, None, Kc, Kc, pos, Kc, Kc, pos, ws)
 
 
 def test_pool_window_cap_and_alignment_rule(fc):

@@ -70,10 +70,12 @@ class Lockstep:
         self.K, self.V, self.pos = st["K"], st["V"], st["pos"]
 
 
-def run_config(fc, cfg, Q_all, K_all, V_all, heads=None, sizes=None, label=""):
+def run_config(fc, cfg, Q_all, K_all, V_all, heads=None, sizes=None, label="", in_place=False):
     """Commit the run's chunks (sizes: tokens per commit, default whole
     chunks) into a KvCache and the oracle side by side.  Q_all, K_all, V_all
-    are device tensors with every head; the oracle reads the sampled heads."""
+    are device tensors with every head; the oracle reads the sampled heads.
+    in_place: each chunk is written into the cache's active rows first and
+    committed where it lies (else the commit copies it in)."""
     dt = K_all.dtype
     H = K_all.shape[0]
     heads = list(range(H)) if heads is None else list(heads)
@@ -89,7 +91,13 @@ def run_config(fc, cfg, Q_all, K_all, V_all, heads=None, sizes=None, label=""):
         Kc = K_all[:, p0:p0 + n].contiguous()
         Vc = V_all[:, p0:p0 + n].contiguous()
         Q = Q_all[c % Q_all.shape[0]]
-        cache.commit(Kc, Vc, Q)
+        if in_place:
+            Ka, Va = cache.active(n)
+            Ka.copy_(Kc)
+            Va.copy_(Vc)
+            cache.commit(None, None, Q, L_c=n)
+        else:
+            cache.commit(Kc, Vc, Q)
         torch.cuda.synchronize()
         ls.step(cache, hK[:, p0:p0 + n], hV[:, p0:p0 + n], p0, Q[heads].cpu(), cfg.B_budget, cfg.lam, cfg.w)
         p0 += n
@@ -136,6 +144,36 @@ def test_ragged_commits(fc, dtype, d):
     pm = torch.cat([before.pos[:, :before.length],
                     torch.arange(p0, total, dtype=torch.int32, device=DEV).expand(cfg.H, -1)], dim=1)
     assert torch.equal(pm.gather(1, out["idx"].long()), cache.pos)
+
+
+def test_in_place_commits_match_copies(fc):
+    # a chunk written into the active rows and committed where it lies gives
+    # the same cache, bit for bit, as the chunk handed over for copying; a
+    # compressing commit moves the clean tokens to the other region
+    cfg = synth.CacheConfig("inplace", H=3, d=128, n_chunks=8, fpc=1, ny=12, nx=10, B_budget=150, B_active=120,
+                            Lq=50, lam=0.4, w=5, dtype="bf16")
+    sizes = [120, 7, 64, 1, 120, 33, 90, 120]
+    say(f"case: cache run, in-place commits against copied ones: {sizes}")
+    total = sum(sizes)
+    Q, K, V = synth.random_kv(cfg.H, cfg.Lq, total, cfg.d, "bf16", seed=21)
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    a = fc.KvCache(cfg.H, cfg.d, cfg.B_budget, cfg.B_active, cfg.Lq, cfg.lam, cfg.w, torch.bfloat16)
+    b = fc.KvCache(cfg.H, cfg.d, cfg.B_budget, cfg.B_active, cfg.Lq, cfg.lam, cfg.w, torch.bfloat16)
+    p0 = 0
+    for n in sizes:
+        Kc, Vc = Kd[:, p0:p0 + n].contiguous(), Vd[:, p0:p0 + n].contiguous()
+        full = a.length + n > cfg.B_budget
+        cur = b.cur
+        a.commit(Kc, Vc, Qd)
+        Ka, Va = b.active(n)
+        Ka.copy_(Kc)
+        Va.copy_(Vc)
+        b.commit(None, None, Qd, L_c=n)
+        torch.cuda.synchronize()
+        assert b.cur == (1 - cur if full else cur)
+        assert a.cur == b.cur and a.length == b.length == min(p0 + n, cfg.B_budget) and b.next_pos == p0 + n
+        assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V) and torch.equal(a.pos, b.pos)
+        p0 += n
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -191,7 +191,8 @@ def test_random_cache_runs(fc, seed):
     total = sum(sizes)
     Q, K, V = synth.random_kv(H, Lq, total, d, dtype, seed=6000 + seed)
     Qs = torch.stack([torch.roll(Q, shifts=c, dims=1) for c in range(3)])
-    cache, _ = run_config(fc, cfg, Qs.to(DEV), K.to(DEV), V.to(DEV), sizes=sizes, label=f"random {seed}")
+    cache, _ = run_config(fc, cfg, Qs.to(DEV), K.to(DEV), V.to(DEV), sizes=sizes, label=f"random {seed}",
+                          in_place=seed % 2 == 1)
     assert cache.length == min(total, B_budget)
 
 
