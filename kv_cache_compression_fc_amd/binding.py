@@ -358,9 +358,28 @@ def fc_chunk_rel_l1_workspace_bytes(p: fc_l1_params, chunk_offsets: Sequence[int
     return int(_lib.fc_chunk_rel_l1_workspace_bytes(ctypes.byref(p), _offsets(chunk_offsets)))
 
 
+# The (m, eps) settings the FlowCache page reports (Key designs item 2): m
+# forced-recompute steps (5 for MAGI-1, 4 for SkyReels-V2) and the reuse
+# threshold of its slow (quality) and fast (speed) settings.
+DECISION_PRESETS = {
+    "magi-slow": (5, 0.01),
+    "magi-fast": (5, 0.015),
+    "skyreels-slow": (4, 0.1),
+    "skyreels-fast": (4, 0.15),
+}
+
+
 class ChunkDecider:
     """Holds the per-chunk state (step, f) and the workspace on the device and
     calls fc_chunk_rel_l1_decide once per denoising step."""
+
+    @classmethod
+    def preset(cls, name: str, chunk_offsets: Sequence[int], dtype: torch.dtype, device="cuda") -> "ChunkDecider":
+        """A decider with one of DECISION_PRESETS' (m, eps) settings."""
+        if name not in DECISION_PRESETS:
+            raise ValueError(f"unknown preset {name!r}; one of {sorted(DECISION_PRESETS)}")
+        m, eps = DECISION_PRESETS[name]
+        return cls(chunk_offsets, m, eps, dtype, device)
 
     def __init__(self, chunk_offsets: Sequence[int], m: int, eps: float, dtype: torch.dtype, device="cuda"):
         self.offsets = [int(x) for x in chunk_offsets]

@@ -328,3 +328,17 @@ def test_noalloc_decision_limits(fc):
                                               None) == fc.FC_ERR_INVALID_ARG
     assert lib.fc_chunk_rel_l1_decide_noalloc(ctypes.byref(fc.fc_l1_params(0, 1, 0.01, fc.FC_BF16)), small, a, a, a,
                                               a, a, None, None) == fc.FC_ERR_INVALID_ARG
+
+
+def test_decision_presets(fc):
+    """The page's settings (FlowCache page, Key designs item 2): m = 5 for
+    MAGI-1 and 4 for SkyReels-V2; eps 0.01 / 0.015 (MAGI slow / fast) and
+    0.1 / 0.15 (SkyReels slow / fast)."""
+    import torch
+    want = {"magi-slow": (5, 0.01), "magi-fast": (5, 0.015), "skyreels-slow": (4, 0.1), "skyreels-fast": (4, 0.15)}
+    assert fc.DECISION_PRESETS == want
+    for name, (m, eps) in want.items():
+        dec = fc.ChunkDecider.preset(name, [0, 100, 250], torch.bfloat16, device="cpu")
+        assert dec.p.m == m and dec.p.eps == pytest.approx(eps, rel=1e-7) and dec.p.n_chunks == 2
+    with pytest.raises(ValueError, match="unknown preset"):
+        fc.ChunkDecider.preset("magi-medium", [0, 100], torch.bfloat16, device="cpu")
