@@ -71,34 +71,25 @@ def time_events(fn, reps: int) -> float:
 
 
 def time_cold(fn, reps: int, scratch):
-    """Average ms per call with the 256 MB MALL (Infinity Cache) flushed first:
+    """Median ms per call with the 256 MB MALL (Infinity Cache) flushed first:
     before each call a 512 MB scratch buffer is read (a sum), which leaves only
     clean scratch lines in the MALL, so the call's own misses cost no
-    write-back of the flush; then the call alone runs between two events
-    (captured in a HIP graph where capture works, so that small kernels see
-    no host launch gaps)."""
+    write-back of the flush; then the call alone runs between two events.
+    Eager launches: the host queues the call's kernels while the GPU is still
+    reading the scratch buffer (about 80 us), so they start back to back; a
+    graph replay would add its own launch latency inside the interval."""
     import torch
-    run, how = fn, "eager"
-    try:
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        g.replay()
-        torch.cuda.synchronize()
-        run, how = g.replay, "graph"
-    except Exception as exc:  # pragma: no cover - capture not available
-        log(f"graph capture failed ({exc}); eager timing")
+    fn()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     sink = torch.empty((), dtype=torch.float32, device=scratch.device)
     for s, e in evs:
         torch.sum(scratch, 0, out=sink)
         s.record()
-        run()
+        fn()
         e.record()
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in evs) / reps, how
+    return statistics.median(s.elapsed_time(e) for s, e in evs), "eager"
 
 
 def workers() -> int:
@@ -271,6 +262,9 @@ def main() -> int:
     ap.add_argument("--loop-lse", type=float, default=0.0, metavar="SECONDS",
                     help="only run importance pass 1 on the long-video shape back to back for SECONDS "
                          "(to read the board's power and clocks meanwhile)")
+    ap.add_argument("--profile-streaming", type=int, default=0, metavar="N",
+                    help="only run the HBM-bound stages (stand-alone redundancy, chunk decision) N times each, "
+                         "the MALL flushed before every call (for kernel traces)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
     args = ap.parse_args()
@@ -343,6 +337,18 @@ def main() -> int:
     offs_c = [i * ccfg.chunk_elems for i in range(ccfg.n_chunks + 1)]
     dec = fc.ChunkDecider(offs_c, ccfg.m, ccfg.eps[0], torch.bfloat16, dev)
     dec.step.copy_(torch.tensor(steps, dtype=torch.int32))
+    if args.profile_streaming > 0:
+        scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB, read before each call
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+        for _ in range(args.profile_streaming):
+            torch.sum(scratch, 0, out=sink)
+            fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws)
+            torch.sum(scratch, 0, out=sink)
+            dec.decide(xt_d, xtm1_d)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_streaming_calls": args.profile_streaming}), flush=True)
+        return 0
 
     out = {"K_out": torch.empty((H, Bp, d), dtype=Kd.dtype, device=dev),
            "V_out": torch.empty((H, Bp, d), dtype=Vd.dtype, device=dev),
@@ -465,7 +471,7 @@ def main() -> int:
         },
         "lambda_sweep": sweep,
         "timing": f"HIP events on the launch stream, {reps} calls each; mall_flushed: 512 MB read before each "
-                  f"call, one call per {how_cold} replay; select_gather includes the redundancy softmax "
+                  f"call, {how_cold} launches, median; select_gather includes the redundancy softmax "
                   f"statistics kernel that fc_kv_compress takes from pass 2 instead",
     }
     for k, v in stages.items():

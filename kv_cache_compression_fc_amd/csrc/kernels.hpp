@@ -69,7 +69,8 @@ hipError_t launch_imp_lse_merge(const float2* part, float* lse, float* nlse2, in
 // -lse2 from a natural-log lse.
 hipError_t launch_imp_nlse2(const float* lse, float* nlse2, int H, int Lq, hipStream_t s);
 // ---- redundancy -------------------------------------------------------------
-// Blocks per head of the two redundancy passes.
+// Blocks per head of the two redundancy passes (at most kRedMaxBlocks each).
+constexpr int kRedMaxBlocks = 64;
 int red_nbu(int Lk);
 int red_nbr(int Lk);
 // Pass A: per-block partial u = sum khat over the block's keys -> u_part[H][nbu][d].

@@ -40,13 +40,31 @@ __device__ __forceinline__ void load_vec<kF32>(const void* p, float* x) {
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
 
+// load_vec with a non-temporal load (rows read once by a streaming pass).
+template <int DT>
+__device__ __forceinline__ void load_vec_stream(const void* p, float* x) {
+    const uint4 u = load_stream16(p);
+    if constexpr (DT == kBF16) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+    }
+}
+
 constexpr int kRedRowsInFlight = 4;  // rows each lane group loads before reducing
 
 // u_out[c] = sum over rows r0 <= j < r1 of khat_j[c] (Kh: the head's rows).
 // Lane groups of kTpr lanes take one row each; the per-lane partials are
 // added across the groups of a wave with shuffles, then across waves in
-// `scratch` (THREADS / 64 * D floats of LDS), in a fixed order.
-template <int DT, int D, int THREADS>
+// `scratch` (THREADS / 64 * D floats of LDS), in a fixed order.  RIF rows per
+// lane group are loaded before they are reduced; STREAM: non-temporal loads.
+template <int DT, int D, int THREADS, int RIF = kRedRowsInFlight, bool STREAM = false>
 __device__ __forceinline__ void red_norm_sum_rows(const char* __restrict__ Kh, int r0, int r1,
                                                   float* __restrict__ scratch, float* __restrict__ u_out) {
     using RL = RowLayout<DT, D, THREADS>;
@@ -55,19 +73,22 @@ __device__ __forceinline__ void red_norm_sum_rows(const char* __restrict__ Kh, i
     float u[RL::kVec];
 #pragma unroll
     for (int v = 0; v < RL::kVec; ++v) u[v] = 0.f;
-    for (int row = r0 + g; row < r1; row += kRedRowsInFlight * RL::kRpi) {
-        float x[kRedRowsInFlight][RL::kVec];
+    for (int row = r0 + g; row < r1; row += RIF * RL::kRpi) {
+        float x[RIF][RL::kVec];
 #pragma unroll
-        for (int i = 0; i < kRedRowsInFlight; ++i) {
+        for (int i = 0; i < RIF; ++i) {
             const int rr = row + i * RL::kRpi;
-            if (rr < r1) load_vec<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
-            else {
+            if (rr < r1) {
+                const char* src = Kh + ((size_t)rr * D + e * RL::kVec) * kE;
+                if constexpr (STREAM) load_vec_stream<DT>(src, x[i]);
+                else load_vec<DT>(src, x[i]);
+            } else {
 #pragma unroll
                 for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;  // contributes nothing to u
             }
         }
 #pragma unroll
-        for (int i = 0; i < kRedRowsInFlight; ++i) {
+        for (int i = 0; i < RIF; ++i) {
             float n2 = 0.f;
 #pragma unroll
             for (int v = 0; v < RL::kVec; ++v) n2 = fmaf(x[i][v], x[i][v], n2);

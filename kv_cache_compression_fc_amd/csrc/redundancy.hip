@@ -4,7 +4,8 @@
 // softmaxed.  With khat_j = k_j / max(||k_j||, 1e-12) and u = sum_i khat_i,
 //     r_j = (1/L_k) sum_{i != j} khat_i . khat_j = (u . khat_j - khat_j . khat_j) / L_k,
 // so no L_k x L_k matrix is formed.  Two streaming passes over K, both
-// HBM-bound (16-byte loads, one row per TPR lanes, wave reductions):
+// HBM-bound (16-byte non-temporal loads, one row per TPR lanes, two rows per
+// lane group in flight, wave reductions):
 //   pass A: per-block partial u (fixed-order reduction, no float atomics;
 //           inside fc_kv_compress it runs as extra workgroups of importance
 //           pass 1 instead);
@@ -19,7 +20,12 @@ namespace fc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsInFlight = kRedRowsInFlight;
+// Rows each lane group loads before reducing them.  Measured on the
+// long-video keys (24 x 129600 rows of 256 B, MALL flushed): 2 rows with
+// non-temporal loads 122 + 149 us for the two passes, against 135 + 170 us
+// with 4 rows and cached loads; 1, 3 and 4 rows, and 96 or 128 workgroups
+// per head, were slower.
+constexpr int kRowsInFlight = 2;
 template <int DT, int D> using RL256 = RowLayout<DT, D, kThreads>;
 
 template <int DT, int D>
@@ -30,8 +36,8 @@ __global__ __launch_bounds__(kThreads) void red_norm_sum_kernel(const void* __re
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
     const int rows = (Lk + nblk - 1) / nblk;
     const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
-    red_norm_sum_rows<DT, D, kThreads>(static_cast<const char*>(K) + (size_t)h * Lk * D * kE, r0, r1, scratch,
-                                       u_part + ((size_t)h * nblk + blk) * D);
+    red_norm_sum_rows<DT, D, kThreads, kRowsInFlight, true>(static_cast<const char*>(K) + (size_t)h * Lk * D * kE,
+                                                            r0, r1, scratch, u_part + ((size_t)h * nblk + blk) * D);
 }
 
 // Online softmax statistics of a block's values, merged over the block.
@@ -66,18 +72,44 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
     __shared__ float upart[kParts][D];
     __shared__ float ush[D];
     const int h = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    const int rows = (Lk + nblk - 1) / nblk;
+    const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
+    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
+    const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
+    auto load_rows = [&](int row, float (&x)[kRowsInFlight][RL::kVec]) {
+#pragma unroll
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int rr = row + i * RL::kRpi;
+            if (rr < r1) {
+                load_vec_stream<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;
+            }
+        }
+    };
+    // the workgroup's first rows are in flight while u is formed
+    float x[kRowsInFlight][RL::kVec];
+    load_rows(r0 + g, x);
     // u = sum of the nbu partials: every thread takes every kParts-th partial
-    // of one column (two independent sums), then the parts are added in order
+    // of one column (two interleaved sums, all loads issued at once), then
+    // the parts are added in order
     {
         const int c = threadIdx.x % D, part = threadIdx.x / D;
         const float* pc = u_part + (size_t)h * nbu * D + c;
-        float a0 = 0.f, a1 = 0.f;
-        int i = part;
-        for (; i + kParts < nbu; i += 2 * kParts) {
-            a0 += pc[(size_t)i * D];
-            a1 += pc[(size_t)(i + kParts) * D];
+        constexpr int kMaxJ = (kRedMaxBlocks / kParts + 1) / 2 * 2;
+        float t[kMaxJ];
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            const int i = part + j * kParts;
+            t[j] = i < nbu ? pc[(size_t)i * D] : 0.f;
         }
-        if (i < nbu) a0 += pc[(size_t)i * D];
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; j += 2) {
+            a0 += t[j];
+            a1 += t[j + 1];
+        }
         upart[part][c] = a0 + a1;
     }
     __syncthreads();
@@ -88,29 +120,15 @@ __global__ __launch_bounds__(kThreads) void red_dot_kernel(const void* __restric
         ush[threadIdx.x] = acc;
     }
     __syncthreads();
-    const int g = threadIdx.x / RL::kTpr, e = threadIdx.x % RL::kTpr;
     float u[RL::kVec];
 #pragma unroll
     for (int v = 0; v < RL::kVec; ++v) u[v] = ush[e * RL::kVec + v];
-
-    const int rows = (Lk + nblk - 1) / nblk;
-    const int r0 = blk * rows, r1 = min(Lk, r0 + rows);
-    const char* Kh = static_cast<const char*>(K) + (size_t)h * Lk * D * kE;
     const float inv_lk = 1.0f / (float)Lk;
     // r_j is a mean of cosines, |r_j| < 1, so sum 2^(r_j log2e - log2e) needs
     // no running maximum: the block's softmax partial is (log2e, s)
     float s = 0.f;
     for (int row = r0 + g; row < r1; row += kRowsInFlight * RL::kRpi) {
-        float x[kRowsInFlight][RL::kVec];
-#pragma unroll
-        for (int i = 0; i < kRowsInFlight; ++i) {
-            const int rr = row + i * RL::kRpi;
-            if (rr < r1) load_vec<DT>(Kh + ((size_t)rr * D + e * RL::kVec) * kE, x[i]);
-            else {
-#pragma unroll
-                for (int v = 0; v < RL::kVec; ++v) x[i][v] = 0.f;
-            }
-        }
+        if (row != r0 + g) load_rows(row, x);
 #pragma unroll
         for (int i = 0; i < kRowsInFlight; ++i) {
             const int rr = row + i * RL::kRpi;
@@ -160,11 +178,11 @@ hipError_t dot_launch(const void* K, const float* u_part, float* r, float2* red_
 
 int red_nbu(int Lk) {
     int n = (Lk + 511) / 512;
-    return n < 1 ? 1 : (n > 64 ? 64 : n);
+    return n < 1 ? 1 : (n > kRedMaxBlocks ? kRedMaxBlocks : n);
 }
 int red_nbr(int Lk) {
     int n = (Lk + 255) / 256;
-    return n < 1 ? 1 : (n > 64 ? 64 : n);
+    return n < 1 ? 1 : (n > kRedMaxBlocks ? kRedMaxBlocks : n);
 }
 
 hipError_t launch_red_norm_sum(int dt, int d, const void* K, float* u_part, int H, int Lk, hipStream_t s) {
