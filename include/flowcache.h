@@ -275,7 +275,8 @@ size_t fc_cache_commit_workspace_bytes(const fc_cache_params* c, int32_t L_q);
  * two regions each other.  *L_clean and *swapped are set when the work has
  * been queued.  Errors as for fc_kv_compress; an L_clean, L_c or pos0 out of
  * range, only one of K_chunk and V_chunk, or a NULL Q or spare region for a
- * commit that compresses, is FC_ERR_INVALID_ARG.
+ * commit that compresses, is FC_ERR_INVALID_ARG, and so is a spare tensor at
+ * the address of a current one (the one overlap the library can see).
  */
 fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean,
                           const void* K_chunk, const void* V_chunk, int32_t L_c, int32_t pos0,

@@ -429,6 +429,10 @@ fc_status fc_cache_commit(const fc_cache_params* c, int32_t* L_clean, const void
         if (Q == nullptr || L_q < 1 || !aligned16(Q)) return FC_ERR_INVALID_ARG;
         if (!K_spare || !V_spare || !aligned16(K_spare) || !aligned16(V_spare)) return FC_ERR_INVALID_ARG;
         if ((pos_cur == nullptr) != (pos_spare == nullptr)) return FC_ERR_INVALID_ARG;
+        // the compression cannot gather into the region it reads
+        if (K_spare == K_cur || V_spare == V_cur || K_spare == V_cur || V_spare == K_cur ||
+            (pos_spare != nullptr && pos_spare == pos_cur))
+            return FC_ERR_INVALID_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int dt = c->dtype == FC_BF16 ? kBF16 : kF32;

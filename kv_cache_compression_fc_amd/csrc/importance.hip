@@ -272,7 +272,10 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_lse_ke
         const int qblk = item % nqb, hs = item / nqb;
         const int split = hs % nsplit, h = hs / nsplit;
 
-        const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x & (kWave - 1);
+        // the wave index as a scalar: the LDS-DMA destinations (M0) then need
+        // no readfirstlane per load (0.3 % off the long-video stage)
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         const int half = lane >> 5;
         const FragOffsets<DT, D, KT> fo(lane);
         const int q = qblk * kRowsPerBlock + wave * 32 + (lane & 31);
@@ -627,7 +630,10 @@ __global__ __launch_bounds__(kThreads, min_waves_per_simd<DT>()) void imp_colsum
         const int kblk = item % nkb, hq = item / nkb;
         const int qs = hq % nqs, h = hq / nqs;
 
-        const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x & (kWave - 1);
+        // the wave index as a scalar: the LDS-DMA destinations (M0) then need
+        // no readfirstlane per load (0.3 % off the long-video stage)
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         const int half = lane >> 5;
         const FragOffsets<DT, D, QT> fo(lane);
         const int key = kblk * kRowsPerBlock + wave * 32 + (lane & 31);

@@ -155,12 +155,16 @@ def test_cache_argument_errors(fc):
     dummy = ctypes.c_void_p(4096)
     need = fc.fc_cache_commit_workspace_bytes(c, 3600)
 
-    def commit(L_clean, L_c, pos0=0, Q=dummy, ws_bytes=need, p=c, K_chunk=dummy, V_chunk=dummy, K_spare=dummy,
-               pos_cur=dummy, pos_spare=dummy):
+    # distinct (never dereferenced) addresses for the two regions
+    K_cur, V_cur, pos_cur0 = ctypes.c_void_p(1 << 16), ctypes.c_void_p(2 << 16), ctypes.c_void_p(3 << 16)
+    K_sp, V_sp, pos_sp0 = ctypes.c_void_p(4 << 16), ctypes.c_void_p(5 << 16), ctypes.c_void_p(6 << 16)
+
+    def commit(L_clean, L_c, pos0=0, Q=dummy, ws_bytes=need, p=c, K_chunk=dummy, V_chunk=dummy, K_spare=K_sp,
+               pos_cur=pos_cur0, pos_spare=pos_sp0):
         n = ctypes.c_int32(L_clean)
         sw = ctypes.c_int32(-7)
-        st = lib.fc_cache_commit(ctypes.byref(p), ctypes.byref(n), K_chunk, V_chunk, L_c, pos0, Q, 3600, dummy,
-                                 dummy, pos_cur, K_spare, dummy, pos_spare, ctypes.byref(sw), dummy, ws_bytes, None)
+        st = lib.fc_cache_commit(ctypes.byref(p), ctypes.byref(n), K_chunk, V_chunk, L_c, pos0, Q, 3600, K_cur,
+                                 V_cur, pos_cur, K_spare, V_sp, pos_spare, ctypes.byref(sw), dummy, ws_bytes, None)
         assert sw.value == -7  # untouched on error
         return st, n.value
 
@@ -180,6 +184,14 @@ def test_cache_argument_errors(fc):
     assert commit(7200, 100, K_spare=None) == (fc.FC_ERR_INVALID_ARG, 7200)
     assert commit(7200, 100, pos_spare=None) == (fc.FC_ERR_INVALID_ARG, 7200)
     assert commit(7200, 100, K_spare=ctypes.c_void_p(4100)) == (fc.FC_ERR_INVALID_ARG, 7200)
+    # the spare region at the current region's address
+    n = ctypes.c_int32(7200)
+    sw = ctypes.c_int32(-7)
+    cur, spare = ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20)
+    assert lib.fc_cache_commit(ctypes.byref(c), ctypes.byref(n), dummy, dummy, 100, 0, dummy, 3600, cur, spare,
+                               None, cur, ctypes.c_void_p(1 << 21), None, ctypes.byref(sw), dummy, need,
+                               None) == fc.FC_ERR_INVALID_ARG
+    assert n.value == 7200 and sw.value == -7
     # a chunk given by one pointer only
     assert commit(0, 100, V_chunk=None) == (fc.FC_ERR_INVALID_ARG, 0)
     assert lib.fc_cache_commit(ctypes.byref(c), None, dummy, dummy, 10, 0, dummy, 3600, dummy, dummy, dummy, dummy,
