@@ -444,6 +444,7 @@ def main() -> int:
 
     qk_flops = 2.0 * H * Lq * Lk * d              # one Q K^T product (the method's own work)
     red_bytes = H * Lk * (d * 2 + 4)              # read K once, write r
+    red_exec_bytes = H * Lk * (2 * d * 2 + 4)     # the two passes: K read twice, r written
     sel_bytes = 8 * H * Lk + 4 * H * Bp + 2 * 2 * H * Bp * d * 2   # imp + r, idx, K/V rows read + written
     l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
     fused_bytes = 3 * ccfg.n_chunks * ccfg.chunk_elems * 2          # X_t and v read, X_{t-1} written
@@ -459,6 +460,7 @@ def main() -> int:
         "select_gather_ms": t_sel, "select_gather_gbps": sel_bytes / (t_sel * 1e-3) / 1e9,
         "select_indices_only_ms": t_sel_idx,
         "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
+        "redundancy_standalone_executed_gbps": red_exec_bytes / (t_red * 1e-3) / 1e9,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "chunk_l1_noalloc_ms": t_noalloc, "chunk_l1_noalloc_gbps": l1_bytes / (t_noalloc * 1e-3) / 1e9,
         "euler_l1_fused_ms": t_fused, "euler_l1_fused_gbps": fused_bytes / (t_fused * 1e-3) / 1e9,
@@ -466,6 +468,8 @@ def main() -> int:
         "history_l1_ms": t_hist, "history_l1_gbps": l1_bytes / (t_hist * 1e-3) / 1e9,
         "mall_flushed": {
             "redundancy_standalone_ms": t_red_c, "redundancy_standalone_gbps": red_bytes / (t_red_c * 1e-3) / 1e9,
+            "redundancy_standalone_executed_gbps": red_exec_bytes / (t_red_c * 1e-3) / 1e9,
+            "per_pass": "profiles/streaming_long_kernel_trace.md (bench.py --profile-streaming under a kernel trace)",
             "select_gather_ms": t_sel_c, "select_gather_gbps": sel_bytes / (t_sel_c * 1e-3) / 1e9,
             "chunk_l1_ms": t_l1_c, "chunk_l1_gbps": l1_bytes / (t_l1_c * 1e-3) / 1e9,
         },
