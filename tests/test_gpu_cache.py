@@ -252,3 +252,30 @@ def test_degenerate_budget_and_positions(fc):
     assert all((p[h][1:] > p[h][:-1]).all() for h in range(H))
     with pytest.raises(fc.FlowCacheError):   # one more token would pass 2^31 - 1
         cache.commit(Kd[:, :1].contiguous(), Vd[:, :1].contiguous(), Q.to(DEV))
+
+
+def test_commit_without_positions(fc):
+    # positions are optional: the same commits with pos_cur = pos_spare = NULL
+    # leave the same K and V as KvCache, which tracks positions
+    H, d, B, Ba = 2, 128, 90, 70
+    sizes = [70, 10, 33, 70, 5]
+    say(f"case: commits without positions, {sizes}")
+    total = sum(sizes)
+    Q, K, V = synth.random_kv(H, 40, total, d, "bf16", seed=31)
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    ref = fc.KvCache(H, d, B, Ba, 40, 0.5, 5, torch.bfloat16)
+    regs = [(torch.zeros((H, B + Ba, d), dtype=torch.bfloat16, device=DEV),
+             torch.zeros((H, B + Ba, d), dtype=torch.bfloat16, device=DEV)) for _ in range(2)]
+    cur, length, p0 = 0, 0, 0
+    for n in sizes:
+        Kc, Vc = Kd[:, p0:p0 + n].contiguous(), Vd[:, p0:p0 + n].contiguous()
+        ref.commit(Kc, Vc, Qd)
+        (Kcur, Vcur), (Ksp, Vsp) = regs[cur], regs[1 - cur]
+        length, swapped = fc.fc_cache_commit(ref.p, length, Kc, Vc, p0, Qd, Kcur, Vcur, None, Ksp, Vsp, None,
+                                             ref.workspace)
+        if swapped:
+            cur = 1 - cur
+        p0 += n
+        torch.cuda.synchronize()
+        assert length == ref.length and cur == ref.cur
+        assert torch.equal(regs[cur][0][:, :length], ref.K) and torch.equal(regs[cur][1][:, :length], ref.V)
