@@ -52,6 +52,43 @@ def test_compress_graph_replays(fc):
             assert torch.equal(out[k], want[k]), f"replay {r}: {k} differs from the eager call"
 
 
+def test_compress_graph_replays_persistent_split(fc):
+    # a shape large enough for the persistent importance passes (their work
+    # counters are zeroed by a kernel each call) and the multi-workgroup
+    # selection (per-workgroup histograms over four launches)
+    H, Lq, Lk, d, B = 8, 2048, 131072, 128, 40000
+    say(f"case: fc_kv_compress captured in a graph (H={H} d={d} bf16 Lq={Lq} Lk={Lk} B={B}), 3 replays")
+    g0 = torch.Generator(device=DEV)
+    g0.manual_seed(5)
+    Q = torch.randn((H, Lq, d), generator=g0, device=DEV).to(torch.bfloat16)
+    K = torch.randn((H, Lk, d), generator=g0, device=DEV).to(torch.bfloat16)
+    V = torch.randn((H, Lk, d), generator=g0, device=DEV).to(torch.bfloat16)
+    lam, w = 0.5, 7
+    p = fc.kv_params(Q, K, B, lam, w)
+    ws = torch.empty(fc.fc_kv_compress_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    want = fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, workspace=ws)
+    torch.cuda.synchronize()
+    out = {k: torch.empty_like(v) for k, v in want.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fc.fc_kv_compress(Q, K, V, B, lam, w, want_scores=True, out=out, workspace=ws)
+    for r in range(3):
+        for v in out.values():
+            v.fill_(0)
+        ws.fill_(0xAB)                       # counters and histograms must be rebuilt by the replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in want:
+            assert torch.equal(out[k], want[k]), f"replay {r}: {k} differs from the eager call"
+
+
 def test_decision_graph_replays(fc):
     say("case: fc_chunk_rel_l1_decide captured in a graph, 6 replays against an eager twin")
     cfg = synth.ChunkConfig("g", n_chunks=5, chunk_elems=20000, N=12, m=2, eps=(0.05,), dtype="bf16", start_stride=0)
