@@ -318,6 +318,13 @@ CACHE_CONFIGS = {
     # and keeps 7200.
     "magi": CacheConfig("magi", H=24, d=128, n_chunks=10, fpc=4, ny=30, nx=30, B_budget=7200, B_active=3600,
                         Lq=3600, lam=0.5, w=7, dtype="bf16"),
+    # Long-video-like run: 24 heads, chunks of 4 latent frames of 45 x 45
+    # (8100 tokens), a budget of four chunks (32400), an active region of
+    # 9000 rows (above the chunk, so the cache's head stride exceeds every
+    # merged length), 8100 queries, six chunks: commits five and six merge
+    # 40500 tokens and keep 32400.
+    "long": CacheConfig("long", H=24, d=128, n_chunks=6, fpc=4, ny=45, nx=45, B_budget=32400, B_active=9000,
+                        Lq=8100, lam=0.5, w=7, dtype="bf16"),
 }
 
 

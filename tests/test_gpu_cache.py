@@ -231,6 +231,31 @@ def test_magi_like_run(fc):
     assert ls.n_comp == cfg.n_chunks - 2
 
 
+def test_long_like_run(fc):
+    # the long-video-like run (24 heads, chunks of 8100, budget 32400, 8100
+    # queries): merged sets of 40500 keys take the multi-workgroup selection
+    # and the persistent pass 1, read with a head stride of 41400 rows; the
+    # oracle follows head 7, the other heads carry seeded N(0,1) values
+    cfg = synth.CACHE_CONFIGS["long"]
+    heads = [7]
+    say("case: cache run, long-video-like (H=24 d=128 bf16, 6 chunks of 8100, budget 32400, active 9000), "
+        "oracle on head 7")
+    T = cfg.tokens_per_chunk
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    K = torch.randn((cfg.H, cfg.n_chunks * T, cfg.d), generator=g, device=DEV).to(torch.bfloat16)
+    V = torch.randn((cfg.H, cfg.n_chunks * T, cfg.d), generator=g, device=DEV).to(torch.bfloat16)
+    Q = torch.randn((cfg.n_chunks, cfg.H, cfg.Lq, cfg.d), generator=g, device=DEV).to(torch.bfloat16)
+    hQ, hK, hV = synth.cache_inputs(cfg, seed=0, heads=heads)
+    for n, h in enumerate(heads):
+        K[h].copy_(hK[n].to(DEV))
+        V[h].copy_(hV[n].to(DEV))
+        Q[:, h].copy_(hQ[:, n].to(DEV))
+    torch.cuda.synchronize()
+    _, ls = run_config(fc, cfg, Q, K, V, heads=heads, label="long", in_place=True)
+    assert ls.n_comp == cfg.n_chunks - 4
+
+
 def test_degenerate_budget_and_positions(fc):
     # a budget of one token, single-token chunks, positions that end at 2^31 - 1
     H, d = 2, 64
