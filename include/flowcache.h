@@ -55,19 +55,23 @@
 extern "C" {
 #endif
 
+/* Both enums carry a last enumerator of 0x7fffffff, so that any int value a
+ * C caller passes is a valid value of the type on the C++ side as well
+ * (such values are answered as unknown or unsupported). */
 typedef enum {
     FC_OK = 0,
     FC_ERR_INVALID_ARG = 1,
     FC_ERR_UNSUPPORTED = 2,
     FC_ERR_WORKSPACE = 3,
-    FC_ERR_HIP = 4
+    FC_ERR_HIP = 4,
+    FC_STATUS_MAX_ENUM = 0x7fffffff
 } fc_status;
 
 /* Static, NUL-terminated description of a status code. */
 const char* fc_status_string(fc_status s);
 
 /* Element type of Q, K, V, K_out, V_out and of the chunk states. */
-typedef enum { FC_F32 = 0, FC_BF16 = 1 } fc_dtype;
+typedef enum { FC_F32 = 0, FC_BF16 = 1, FC_DTYPE_MAX_ENUM = 0x7fffffff } fc_dtype;
 
 /* ------------------------------------------------------------------------ */
 /* Joint importance-redundancy KV compression (Key designs, item 3)         */

@@ -242,6 +242,7 @@ const char* fc_status_string(fc_status s) {
         case FC_ERR_UNSUPPORTED: return "unsupported configuration";
         case FC_ERR_WORKSPACE: return "workspace missing or too small";
         case FC_ERR_HIP: return "HIP launch failed";
+        default: break;
     }
     return "unknown status";
 }
