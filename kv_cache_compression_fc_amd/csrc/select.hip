@@ -6,8 +6,9 @@
 // and each head keeps its B' = min(B, L) best tokens (flowchart under
 // 整体框架: cache full -> joint score -> top-B per head).
 //
-// One 1024-thread workgroup per head does the whole selection, exactly, on
-// the float32 scores.  Each score becomes an order-preserving uint32 key;
+// Heads of up to one chunk of keys (sel_head_kernel): one 1024-thread
+// workgroup per head does the whole selection, exactly, on the float32
+// scores.  Each score becomes an order-preserving uint32 key;
 // three radix rounds (8 + 12 + 12 bits) with LDS histograms find the B'-th
 // largest key T and the number q of keys equal to T that fit.  The scores of
 // one head sit in a narrow range, so the top key bits (sign and exponent) put
@@ -18,9 +19,11 @@
 // indices ascending.  Keys are processed in chunks of 18 consecutive keys per
 // thread, staged through LDS so that every global access is coalesced; a head
 // that fits one chunk keeps its keys in LDS between the passes, a longer one
-// re-reads them from the workspace.  No global atomics: the result is
-// deterministic.  A gather kernel with one block per 32 kept rows then copies
-// their K and V rows.
+// re-reads them from the workspace.  Longer heads take the split selection
+// further down (several workgroups per head, four 8-bit radix rounds over
+// per-workgroup histograms, one launch each).  No global atomics: the result
+// is deterministic.  A gather kernel with one kept row per lane group then
+// copies their K and V rows.
 #include <type_traits>
 
 #include "common.hpp"
