@@ -26,7 +26,7 @@
  *     anything is queued, and return an error code synchronously.
  *   - Outputs must not alias inputs.  Tensors are dense and row-contiguous.
  *   - Alignment: the base pointers of the row tensors (Q, K, V, K_out,
- *     V_out, K_chunk, V_chunk, K_clean, V_clean) and of the chunk states
+ *     V_out, K_chunk, V_chunk, K_cur, V_cur, K_spare, V_spare) and of the chunk states
  *     (X_t, X_tm1, v, X_next, h_prev, h_cur) must be 16-byte aligned (every
  *     hipMalloc or torch allocation is; a view that starts inside a row may
  *     not be).  Any other base is FC_ERR_INVALID_ARG.  Float and int32
@@ -42,8 +42,9 @@
  *     failed).  No exception crosses the ABI.  NaN/Inf inputs are not
  *     supported.
  *   - The library keeps no state between calls (apart from a per-device
- *     cache of the importance kernels' occupancy, filled on first use); calls
- *     on different streams with different workspaces may run concurrently.
+ *     cache of the importance kernels' occupancy, filled on first use, and
+ *     the device scratch array of fc_chunk_rel_l1_decide_noalloc); calls on
+ *     different streams with different workspaces may run concurrently.
  */
 #ifndef FLOWCACHE_H
 #define FLOWCACHE_H
