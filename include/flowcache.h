@@ -28,9 +28,8 @@
  *   - Alignment: the base pointers of the row tensors (Q, K, V, K_out,
  *     V_out, K_chunk, V_chunk, K_cur, V_cur, K_spare, V_spare) and of the
  *     chunk states (X_t, X_tm1, v, X_next, h_prev, h_cur) must be 16-byte
- *     aligned (every
- *     hipMalloc or torch allocation is; a view that starts inside a row may
- *     not be).  Any other base is FC_ERR_INVALID_ARG.  Float and int32
+ *     aligned (every hipMalloc or torch allocation is; a view that starts
+ *     inside a row may not be).  Any other base is FC_ERR_INVALID_ARG.  Float and int32
  *     arrays (imp, r, lse, scores, idx, step, f, ...) need only their
  *     natural alignment.
  *   - Errors: FC_ERR_INVALID_ARG (null required pointer, sizes < 1, lambda not
