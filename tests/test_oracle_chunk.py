@@ -159,6 +159,48 @@ def test_euler_product_and_sum_rounded_separately():
     assert exact == 2.0 ** -46
 
 
+def test_euler_recipe_against_the_update_rounded_once():
+    # The page's update is X_{t-1} = X_t + v dt.  Computed in fp64 and rounded
+    # once to the storage type it is the plain definition; the recipe rounds
+    # the product and the sum to float32 first.  float32 storage: the two
+    # roundings stay within one float32 ulp of the product plus one of the
+    # result.  bf16 storage: the float32 error, then at most one bf16 ulp from
+    # rounding twice; that happens only when the float32 sum lies within its
+    # own error of a bf16 half-way point (or the sum nearly cancels), which
+    # random data rarely hits.
+    import torch
+    rng = np.random.default_rng(3)
+    n = 200_000
+    x = rng.standard_normal(n).astype(np.float32) * 4
+    v = rng.standard_normal(n).astype(np.float32)
+    offs, dts = [0, 70_000, 150_000, n], [-0.0371, -0.2, -1.0 / 3.0]
+    exact = np.empty(n)
+    for i in range(3):
+        s, e = offs[i], offs[i + 1]
+        exact[s:e] = x[s:e].astype(np.float64) + v[s:e].astype(np.float64) * np.float64(np.float32(dts[i]))
+    y32 = oracle.euler_step(torch.from_numpy(x), torch.from_numpy(v), offs, dts, [True] * 3).double().numpy()
+    prod = np.concatenate([np.abs(v[offs[i]:offs[i + 1]].astype(np.float64) * np.float32(dts[i])) for i in range(3)])
+    ulp = lambda a: np.spacing(np.abs(a).astype(np.float32)).astype(np.float64)
+    assert (np.abs(y32 - exact) <= ulp(prod) + ulp(exact)).all()
+    assert np.mean(y32 == exact.astype(np.float32)) > 0.9   # most land on the once-rounded value
+
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    vb = torch.from_numpy(v).to(torch.bfloat16)
+    xe, ve = xb.double().numpy(), vb.double().numpy()
+    once = np.empty(n)
+    for i in range(3):
+        s, e = offs[i], offs[i + 1]
+        once[s:e] = xe[s:e] + ve[s:e] * np.float64(np.float32(dts[i]))
+    once_b = torch.from_numpy(once).to(torch.bfloat16).double().numpy()   # rounded once, fp64 -> bf16
+    yb = oracle.euler_step(xb, vb, offs, dts, [True] * 3).double().numpy()
+    diff = yb != once_b
+    bf16_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(once_b), 2.0 ** -126))) - 7)
+    prod_b = np.concatenate([np.abs(ve[offs[i]:offs[i + 1]] * np.float32(dts[i])) for i in range(3)])
+    bound = bf16_ulp + ulp(prod_b) + ulp(once)
+    assert (np.abs(yb - once_b)[diff] <= bound[diff]).all()
+    assert diff.mean() < 1e-3
+
+
 def test_euler_inactive_chunks_keep_their_values():
     import torch
     x = torch.arange(10, dtype=torch.float32)
