@@ -263,8 +263,9 @@ def main() -> int:
                     help="only run importance pass 1 on the long-video shape back to back for SECONDS "
                          "(to read the board's power and clocks meanwhile)")
     ap.add_argument("--profile-streaming", type=int, default=0, metavar="N",
-                    help="only run the HBM-bound stages (stand-alone redundancy, chunk decision) N times each, "
-                         "the MALL flushed before every call (for kernel traces)")
+                    help="only run the HBM-bound stages (stand-alone redundancy, chunk decision, select + "
+                         "gather) N times each, the MALL flushed before every call (for kernel traces and "
+                         "HBM counters)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) to calibrate HBM counters")
     args = ap.parse_args()
@@ -341,11 +342,14 @@ def main() -> int:
         scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB, read before each call
         sink = torch.empty((), dtype=torch.float32, device=dev)
         r = torch.empty((H, Lk), dtype=torch.float32, device=dev)
+        imp, r_sel = fc.fc_kv_importance_redundancy(Qd, Kd, workspace=ws)
         for _ in range(args.profile_streaming):
             torch.sum(scratch, 0, out=sink)
             fc.fc_kv_redundancy(Kd, r_out=r, workspace=ws)
             torch.sum(scratch, 0, out=sink)
             dec.decide(xt_d, xtm1_d)
+            torch.sum(scratch, 0, out=sink)
+            fc.fc_kv_select(imp, r_sel, B, lam, w, Kd, Vd, want_scores=False, workspace=ws)
         torch.cuda.synchronize()
         print(json.dumps({"profile_streaming_calls": args.profile_streaming}), flush=True)
         return 0
