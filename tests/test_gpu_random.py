@@ -1,6 +1,7 @@
-"""Seeded random sweeps through the C ABI against the fp64 oracle: small
+"""Seeded random sweeps through the C ABI against the fp64 oracle:
 compressions over every dtype, head size, window, lambda and temperature
-the boundary accepts (with one-query, one-key and budget-above-L_k corners),
+the boundary accepts (small ones, wider ones up to 700 queries and 60000
+keys, and one-query, one-key and budget-above-L_k corners),
 chunk decisions (chunkwise, fused Euler, uniform, history-guided) over
 random, unaligned chunk tables with random states, step counters and
 accumulators, and cache runs with random budgets and commit sizes.  The
@@ -45,6 +46,27 @@ def kv_configs(n, seed):
     return out
 
 
+def wide_configs(n, seed):
+    """Larger and more varied shapes: up to 700 queries, 6 heads and 60000
+    keys (a third of them past one 18432-key chunk), windows up to 129."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = ("bf16", "f32")[int(rng.integers(2))] if rng.uniform() < 0.5 else "bf16"
+        d = (64, 128)[int(rng.integers(2))]
+        H = int(rng.integers(1, 7))
+        Lq = 1 if rng.uniform() < 0.08 else int(rng.integers(2, 700))
+        Lk = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(5000, 20000)),
+                             int(rng.integers(18000, 60000))]))
+        B = int(rng.integers(1, Lk + 50))
+        w = int(rng.choice([1, 3, 5, 7, 9, 15, 33, 129]))
+        u = rng.uniform()
+        lam = 0.0 if u < 0.1 else (1.0 if u < 0.2 else round(float(rng.uniform()), 3))
+        scale = 0.0 if rng.uniform() < 0.5 else round(float(rng.uniform(0.02, 0.3)), 4)
+        out.append((dtype, d, H, Lq, Lk, B, w, lam, scale, 5000 + i))
+    return out
+
+
 # shapes whose heads exceed one 18432-key chunk (the split selection), small
 # query counts so the oracle stays fast
 SPLIT = [
@@ -65,7 +87,7 @@ CORNERS = [
 ]
 
 
-@pytest.mark.parametrize("dtype,d,H,Lq,Lk,B,w,lam,scale,seed", kv_configs(16, 2026) + CORNERS + SPLIT)
+@pytest.mark.parametrize("dtype,d,H,Lq,Lk,B,w,lam,scale,seed", kv_configs(16, 2026) + CORNERS + SPLIT + wide_configs(64, 11))
 def test_random_compress(fc, dtype, d, H, Lq, Lk, B, w, lam, scale, seed):
     say(f"case: {dtype} d={d} H={H} Lq={Lq} Lk={Lk} B={B} w={w} lambda={lam} scale={scale} seed={seed}")
     Q, K, V = synth.random_kv(H, Lq, Lk, d, dtype, seed=seed)
