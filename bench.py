@@ -70,6 +70,28 @@ def time_events(fn, reps: int) -> float:
     return s.elapsed_time(e) / reps
 
 
+def time_paired_diff(fa, fb, pairs: int) -> float:
+    """Median over pairs of (ms of one fa call - ms of the fb call right after
+    it), HIP events around each call on the current stream: the clock drifts
+    of a power-capped chip cancel inside a pair, which a difference of two
+    separately timed averages does not."""
+    import torch
+    fa()
+    fb()
+    torch.cuda.synchronize()
+    diffs = []
+    for _ in range(pairs):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        fa()
+        ev[1].record()
+        fb()
+        ev[2].record()
+        ev[2].synchronize()
+        diffs.append(ev[0].elapsed_time(ev[1]) - ev[1].elapsed_time(ev[2]))
+    return statistics.median(diffs)
+
+
 def time_cold(fn, reps: int, scratch):
     """Median ms per call with the 256 MB MALL (Infinity Cache) flushed first:
     before each call a 512 MB scratch buffer is read (a sum), which leaves only
@@ -233,14 +255,18 @@ def other_shapes(fc, synth, dev, reps: int):
         o = {"K_out": torch.empty((H, B, d), dtype=K.dtype, device=dev),
              "V_out": torch.empty((H, B, d), dtype=V.dtype, device=dev),
              "idx": torch.empty((H, B), dtype=torch.int32, device=dev)}
-        t = time_events(lambda: fc.fc_kv_compress(Q, K, V, B, lam, cfg.w, out=o, workspace=ws), reps)
-        t_imp = time_events(lambda: fc.fc_kv_importance_redundancy(Q, K, workspace=ws), reps)
+        comp = lambda: fc.fc_kv_compress(Q, K, V, B, lam, cfg.w, out=o, workspace=ws)
+        imp_o, r_o = (torch.empty((H, Lk), dtype=torch.float32, device=dev) for _ in range(2))
+        imp_only = lambda: fc.fc_kv_importance_redundancy(Q, K, imp_out=imp_o, r_out=r_o, workspace=ws)
+        t = time_events(comp, reps)
+        t_imp = time_events(imp_only, reps)
+        t_sel = time_paired_diff(comp, imp_only, max(reps, 10))
         flops = 2.0 * H * Lq * Lk * d   # Q K^T once
         out[name] = {"H": H, "L_q": Lq, "L_k": Lk, "B_budget": B, "compress_ms": t,
                      "token_heads_per_s": H * Lk / (t * 1e-3), "tokens_per_s_per_head": Lk / (t * 1e-3),
                      "importance_stage_ms": t_imp,
                      "importance_algorithmic_tflops": flops / (t_imp * 1e-3) / 1e12,
-                     "select_gather_in_compress_ms": t - t_imp, "data": data}
+                     "select_gather_in_compress_ms": t_sel, "data": data}
         del Q, K, V, ws, o
         torch.cuda.empty_cache()
     return out
@@ -453,7 +479,11 @@ def main() -> int:
     l1_bytes = 2 * ccfg.n_chunks * ccfg.chunk_elems * 2             # both states, bf16
     fused_bytes = 3 * ccfg.n_chunks * ccfg.chunk_elems * 2          # X_t and v read, X_{t-1} written
     imp_tflops = qk_flops / (t_imp * 1e-3) / 1e12
-    sel_in_step = t_compress - t_imp
+    # the selection and gather inside the compression: the compression minus
+    # its importance stage, timed in alternating pairs
+    sel_in_step = time_paired_diff(lambda: fc.fc_kv_compress(Qd, Kd, Vd, B, lam, w, out=out, workspace=ws),
+                                   lambda: fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws),
+                                   max(reps, 10))
     stages = {
         "importance_stage_ms": t_imp, "importance_algorithmic_tflops": imp_tflops,
         "importance_executed_tflops": 2 * imp_tflops,
@@ -480,7 +510,9 @@ def main() -> int:
         "lambda_sweep": sweep,
         "timing": f"HIP events on the launch stream, {reps} calls each; mall_flushed: 512 MB read before each "
                   f"call, {how_cold} launches, median; select_gather includes the redundancy softmax "
-                  f"statistics kernel that fc_kv_compress takes from pass 2 instead",
+                  f"statistics kernel that fc_kv_compress takes from pass 2 instead; "
+                  f"select_gather_in_compress: median over alternating pairs of (compression - its "
+                  f"importance stage)",
     }
     for k, v in stages.items():
         log(f"  {k}: {v}")
