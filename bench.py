@@ -426,6 +426,16 @@ def main() -> int:
     # the two passes alone (without the redundancy), for the per-pass rates
     t_lse = time_events(lambda: fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws), reps)
     t_colsum = time_events(lambda: fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp, workspace=ws), reps)
+    # what the redundancy adds inside the importance stage (pass A in pass 1's
+    # launch, pass B in pass 2's): the stage minus the two passes without it,
+    # timed in alternating pairs
+    imp_plain = torch.empty_like(imp)
+
+    def passes_alone():
+        fc.fc_kv_importance_lse(Qd, Kd, lse_out=lse, workspace=ws)
+        fc.fc_kv_importance_colsum(Qd, Kd, lse, imp_out=imp_plain, workspace=ws)
+    t_red_in = time_paired_diff(lambda: fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws),
+                                passes_alone, max(reps, 10))
     fc.fc_kv_importance_redundancy(Qd, Kd, imp_out=imp, r_out=r, workspace=ws)
     t_red = time_events(lambda: fc.fc_kv_redundancy(Kd, r_out=torch.empty_like(r), workspace=ws), reps)
     t_sel = time_events(lambda: fc.fc_kv_select(imp, r, B, lam, w, Kd, Vd, want_scores=False, workspace=ws), reps)
@@ -495,6 +505,8 @@ def main() -> int:
         "select_indices_only_ms": t_sel_idx,
         "redundancy_standalone_ms": t_red, "redundancy_standalone_gbps": red_bytes / (t_red * 1e-3) / 1e9,
         "redundancy_standalone_executed_gbps": red_exec_bytes / (t_red * 1e-3) / 1e9,
+        "redundancy_in_importance_ms": t_red_in,
+        "redundancy_in_importance_gbps": red_bytes / (t_red_in * 1e-3) / 1e9 if t_red_in > 0 else None,
         "compress_ms": t_compress, "chunk_l1_ms": t_l1, "chunk_l1_gbps": l1_bytes / (t_l1 * 1e-3) / 1e9,
         "chunk_l1_noalloc_ms": t_noalloc, "chunk_l1_noalloc_gbps": l1_bytes / (t_noalloc * 1e-3) / 1e9,
         "euler_l1_fused_ms": t_fused, "euler_l1_fused_gbps": fused_bytes / (t_fused * 1e-3) / 1e9,
@@ -512,7 +524,8 @@ def main() -> int:
                   f"call, {how_cold} launches, median; select_gather includes the redundancy softmax "
                   f"statistics kernel that fc_kv_compress takes from pass 2 instead; "
                   f"select_gather_in_compress: median over alternating pairs of (compression - its "
-                  f"importance stage)",
+                  f"importance stage); redundancy_in_importance: likewise (importance stage - its two passes "
+                  f"without the redundancy)",
     }
     for k, v in stages.items():
         log(f"  {k}: {v}")
